@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE FFN layer on one MI355X, against its roofline.
+
+One step = one pass of the whole layer (routing: top-k, histogram, scan,
+scatter, block map; expert FFN: gate/up, SwiGLU, down, weighted combine with
+the shared expert) over one batch of synthetic input already resident in HBM.
+
+Primary line (`value`): batch-1 decode, T = 1 token per step, d = 2048,
+E = 256, top-8 + shared, F = Fs = 512, int4 groups of 64, cycling through 40
+distinct layer weight sets (455 MB each, 18.2 GB in all) so that weights
+stream from HBM and not from cache; each step has its own x and logits.  The
+K timed steps are one HIP graph of K layer calls.
+
+Second object (`prefill`): T = 4096 tokens with Zipf-skewed routing, one
+weight set, timed the same way.
+
+Per-kernel durations come from HIP start/stop events of each dispatch
+(moe_layer_timed launches every kernel through hipExtLaunchKernel with an
+event pair), taken on the same K steps run eagerly right after the timed
+graph replay.  `cpu_baseline` times
+the fp64 CPU oracle (test infrastructure) on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
+METRIC = "MoE-layer tokens/s, prefill T=4096 & decode T=1; % of MFMA/HBM peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+def make_events(n):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()  # materialise the underlying hipEvent_t
+    torch.cuda.synchronize()
+    return evs
+
+
+def gateup_decode_bytes(dims):
+    """Algorithmic bytes of the decode gate/up kernel: packed codes + bf16
+    scale/bias of gate and up for the k routed and the shared expert, x,
+    the logits row, and the fp32 h it writes."""
+    per_row = dims.d // 2 + 2 * 2 * (dims.d // dims.G)
+    w = 2 * per_row * (dims.k * dims.F + dims.Fs)
+    return w + dims.d * 2 + dims.E * 4 + (dims.k * dims.F + dims.Fs) * 4
+
+
+def decode_layer_bytes(dims):
+    """Algorithmic bytes of one decode layer: weights of the k + 1 experts
+    used (codes + scale/bias of gate, up, down), x and y."""
+    gu = dims.d // 2 + 4 * (dims.d // dims.G)
+    dn_r = dims.F // 2 + 4 * (dims.F // dims.G)
+    dn_s = dims.Fs // 2 + 4 * (dims.Fs // dims.G)
+    w = 2 * gu * (dims.k * dims.F + dims.Fs) + dims.d * (dims.k * dn_r + dn_s)
+    return w + 2 * dims.d * 2
+
+
+def gateup_flops(dims):
+    """Useful matrix-core flops of the gate/up GEMM: 2 flops x 2 matrices x d
+    for every (row, column) of the routed rows and the shared rows."""
+    return 4 * dims.d * (dims.T * dims.k * dims.F + dims.T * dims.Fs)
+
+
+def layer_flops(dims):
+    return dims.T * (dims.k * 6 * dims.d * dims.F + 6 * dims.d * dims.Fs)
+
+
+def run_timed(B, dm, calls, steps, warmup):
+    """calls[i] = (logits, x, weights_struct, y) for step i % len(calls).
+
+    Timed region: one HIP graph of `steps` consecutive layer calls, replayed
+    once untimed (upload) and once timed between device synchronisations.
+    Per-kernel times: right after, the same `steps` calls eagerly through
+    moe_layer_timed, whose kernels are launched with start/stop events
+    (hipExtLaunchKernel) on the launch stream.  Returns (seconds, mean ms per
+    kernel)."""
+    import torch
+    nk = B.moe_layer_kernels(dm)
+    r = B.alloc_routing(dm)
+    ws = B.alloc_workspace(dm)
+    for i in range(warmup):
+        lg, x, w, y = calls[i % len(calls)]
+        B.moe_layer(dm, lg, x, w, r, y, ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                lg, x, w, y = calls[i % len(calls)]
+                B.moe_layer(dm, lg, x, w, r, y, ws, stream=stream)
+    torch.cuda.synchronize()
+    g.replay()  # untimed: the first replay uploads the graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    evs = [make_events(2 * nk) for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            lg, x, w, y = calls[i % len(calls)]
+            B.moe_layer_timed(dm, lg, x, w, r, y, ws, [e.cuda_event for e in evs[i]], stream=stream)
+    torch.cuda.synchronize()
+    per_kernel = [sum(ev[2 * j].elapsed_time(ev[2 * j + 1]) for ev in evs) / steps for j in range(nk)]
+    return t1 - t0, per_kernel
+
+
+def bench_decode(B, wl, args):
+    import torch
+    name = "c1_decode"
+    dims = wl.CONFIGS[name]
+    seed = wl.SEED_OF[name]
+    nsets = wl.DECODE_WEIGHT_SETS
+    dm = B.make_dims(dims)
+    sets, host_sets = [], []
+    t = time.time()
+    for s in range(nsets):
+        W = wl.make_weights(dims, seed, s)
+        wd = {m: {f: to_dev(W[m][f]) for f in ("q", "s", "b")} for m in wl.MATS}
+        sets.append((wd, B.weights_struct(wd)))
+        if s < 2:
+            host_sets.append(W)
+        if s % 10 == 9:
+            log(f"decode: {s + 1}/{nsets} weight sets resident ({time.time() - t:.0f} s)")
+    calls, host_inputs = [], []
+    for s in range(nsets):
+        c = wl.make_case(dims, seed=seed, index=s, weights=False)
+        y = torch.empty((1, dims.d), dtype=torch.int16, device="cuda")
+        calls.append((to_dev(c["logits"]), to_dev(c["x"]), sets[s][1], y))
+        host_inputs.append(c)
+    log("decode: capturing and timing")
+    sec, per_kernel = run_timed(B, dm, calls, args.steps, args.warmup)
+    value = args.steps / sec
+    gu_ms = per_kernel[0]
+    gu_bytes = gateup_decode_bytes(dims)
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    out = {
+        "value": value,
+        "ms_per_step": sec * 1e3 / args.steps,
+        "per_kernel_ms": {"decode_gateup": per_kernel[0], "decode_down": per_kernel[1]},
+        "layer_bytes": decode_layer_bytes(dims),
+        "layer_gbs": decode_layer_bytes(dims) / (sec / args.steps) / 1e9,
+        "roofline": {"bound": "hbm", "kernel": "decode_gateup_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": gu_bytes, "avg_launch_ms": gu_ms},
+    }
+    log(f"decode: {value:.0f} tok/s, {out['ms_per_step'] * 1e3:.2f} us/step, gate/up {gu_ms * 1e3:.2f} us "
+        f"({achieved:.0f} GB/s), down {per_kernel[1] * 1e3:.2f} us")
+    del sets, calls
+    torch.cuda.empty_cache()
+    return out, (dims, host_sets, host_inputs)
+
+
+def bench_prefill(B, wl, args):
+    import torch
+    name = "c3_prefill4096_zipf"
+    c = wl.make_case(name)
+    dims = c["dims"]
+    dm = B.make_dims(dims)
+    wd = {m: {f: to_dev(c["w"][m][f]) for f in ("q", "s", "b")} for m in wl.MATS}
+    y = torch.empty((dims.T, dims.d), dtype=torch.int16, device="cuda")
+    calls = [(to_dev(c["logits"]), to_dev(c["x"]), B.weights_struct(wd), y)]
+    log("prefill: capturing and timing")
+    sec, per_kernel = run_timed(B, dm, calls, args.prefill_steps, 3)
+    names = ["route_topk", "route_scan", "route_scatter", "gateup_gemm", "down_gemm", "combine"]
+    value = dims.T * args.prefill_steps / sec
+    gu_ms = per_kernel[3]
+    fl = gateup_flops(dims)
+    achieved = fl / (gu_ms * 1e-3) / 1e12
+    ms = sec * 1e3 / args.prefill_steps
+    out = {
+        "value": value, "unit": "tokens/s", "ms_per_step": ms, "steps": args.prefill_steps,
+        "dtype": "bf16",
+        "config": {"workload": "prefill T=4096 Zipf(1)-skewed routing, d=2048, E=256, top-8 + shared, "
+                               "F=Fs=512, int4 G=64, one weight set", "T": dims.T},
+        "per_kernel_ms": dict(zip(names, per_kernel)),
+        "layer_tflops": layer_flops(dims) / (ms * 1e-3) / 1e12,
+        "layer_mfma_frac": layer_flops(dims) / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+        "roofline": {"bound": "mfma", "kernel": "moe_gateup_kernel", "achieved": achieved,
+                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFS,
+                     "traffic": None, "flops_per_launch": fl, "avg_launch_ms": gu_ms},
+    }
+    log(f"prefill: {value / 1e6:.2f} M tok/s, {ms * 1e3:.1f} us/step, kernels "
+        + ", ".join(f"{n} {t * 1e3:.1f}us" for n, t in zip(names, per_kernel)))
+    return out, c
+
+
+def cpu_baseline_decode(wl, host, seconds):
+    import oracle
+    dims, host_sets, host_inputs = host
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        c = host_inputs[n % len(host_inputs)]
+        r = oracle.route(c["logits"], dims.k, 32)
+        oracle.ffn(dims, c["x"], host_sets[n % len(host_sets)], r["ids"], r["w"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} decode steps (T=1, route + fp64 FFN), 2 weight sets held in host memory; "
+                      "one token per call, so the oracle's token loop runs on one thread"}
+
+
+def cpu_baseline_prefill(wl, c, seconds):
+    import oracle
+    dims = c["dims"]
+    t0 = time.perf_counter()
+    r = oracle.route(c["logits"], dims.k, 128)
+    ntok, n = 0, 64
+    while True:
+        toks = list(range(ntok, ntok + n))
+        oracle.ffn(dims, c["x"], c["w"], r["ids"], r["w"], tokens=toks)
+        ntok += n
+        el = time.perf_counter() - t0
+        if el >= seconds or ntok + n > dims.T:
+            break
+    return {"value": ntok / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"routing of all {dims.T} tokens + fp64 FFN of the first {ntok} tokens of the "
+                      "T=4096 Zipf workload (OpenMP over tokens)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=40, help="untimed decode steps")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_moe_expert_03_amd import binding as B
+    from bit_moe_expert_03_amd import workload as wl
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()  # fails loudly if the HIP library is not built
+
+    dec, host = bench_decode(B, wl, args)
+    pre = c3 = None
+    if not args.no_prefill:
+        pre, c3 = bench_prefill(B, wl, args)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline_decode(wl, host, args.cpu_seconds)
+        if pre is not None:
+            pre["cpu_baseline"] = cpu_baseline_prefill(wl, c3, args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": dec["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode T=1, d=2048, E=256, top-8 + shared, F=Fs=512, int4 G=64, "
+                               "40 layer weight sets rotated per step", "T": 1, "weight_sets": 40},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "decode_detail": {k: dec[k] for k in ("per_kernel_ms", "layer_bytes", "layer_gbs")},
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

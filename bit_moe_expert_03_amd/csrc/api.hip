@@ -1,0 +1,288 @@
+// C ABI of the MoE layer: host-side validation, workspace carving and the
+// launch sequence.  Nothing here touches the device except kernel launches
+// on the caller's stream; no host synchronisation, no device-to-host copy
+// (the Lily pages attribute a large prefill gain to keeping the routing
+// metadata on the GPU with no host round trip: page "Perplexity's Lily Beats
+// MLX-LM by 1.35x Running Qwen3.6 on Apple Silicon", section "Prefill
+// optimizations", second bullet).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local std::string g_last_error;
+
+static moe_status fail(moe_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static int pick_tile_m(int64_t A, int E)
+{
+    const int64_t per_expert = A / (E > 0 ? E : 1);
+    if (per_expert <= 32) return 32;
+    if (per_expert <= 64) return 64;
+    return 128;
+}
+
+static bool mult_ok(int v, int G) { return v > 0 && v <= 16384 && v % 64 == 0 && v % G == 0; }
+
+moe_status make_plan(const moe_dims *dm, Plan *p, const char **why)
+{
+    if (!dm) { *why = "dims is NULL"; return MOE_ERR_ARG; }
+    const moe_dims &d = *dm;
+    if (d.T < 0 || d.T > (1 << 22)) { *why = "T outside [0, 2^22]"; return MOE_ERR_SHAPE; }
+    if (d.E < 1 || d.E > kMaxE) { *why = "E outside [1, 256]"; return MOE_ERR_SHAPE; }
+    if (d.k < 1 || d.k > d.E) { *why = "k outside [1, E]"; return MOE_ERR_SHAPE; }
+    if ((int64_t)d.T * d.k >= ((int64_t)1 << 31)) { *why = "T*k >= 2^31"; return MOE_ERR_SHAPE; }
+    if (d.G != 32 && d.G != 64 && d.G != 128) { *why = "G not in {32, 64, 128}"; return MOE_ERR_SHAPE; }
+    if (!mult_ok(d.d, d.G)) { *why = "d must be a positive multiple of 64 and of G, <= 16384"; return MOE_ERR_SHAPE; }
+    if (!mult_ok(d.F, d.G)) { *why = "F must be a positive multiple of 64 and of G, <= 16384"; return MOE_ERR_SHAPE; }
+    if (!mult_ok(d.Fs, d.G)) { *why = "Fs must be a positive multiple of 64 and of G, <= 16384"; return MOE_ERR_SHAPE; }
+    if (d.tile_m != 0 && d.tile_m != 32 && d.tile_m != 64 && d.tile_m != 128) {
+        *why = "tile_m not in {0, 32, 64, 128}";
+        return MOE_ERR_SHAPE;
+    }
+    p->T = d.T; p->d = d.d; p->E = d.E; p->k = d.k; p->F = d.F; p->Fs = d.Fs; p->G = d.G;
+    p->A = (int64_t)d.T * d.k;
+    p->tile_m = d.tile_m ? d.tile_m : pick_tile_m(p->A, d.E);
+    // route chunks: at most kRouteMaxBlocks blocks, >= 16 tokens (one per wave)
+    int tb = (int)((d.T + kRouteMaxBlocks - 1) / kRouteMaxBlocks);
+    tb = ((tb + 15) / 16) * 16;
+    if (tb < 16) tb = 16;
+    p->route_tb = tb;
+    p->route_nb = (d.T + tb - 1) / tb;
+    p->max_tiles = (p->A + p->tile_m - 1) / p->tile_m + (p->A < d.E ? p->A : d.E);
+    const int Fmax = d.F > d.Fs ? d.F : d.Fs;
+    size_t off = 0;
+    p->off_hist = off; off = align_up(off + (size_t)d.E * p->route_nb * 4);
+    p->off_hr = off;   off = align_up(off + (size_t)p->A * d.F * 2);
+    p->off_hs = off;   off = align_up(off + (size_t)d.T * d.Fs * 2);
+    p->off_obuf = off; off = align_up(off + (size_t)(p->A + d.T) * d.d * 2);
+    p->off_dech = off; off = align_up(off + (size_t)(d.k + 1) * Fmax * 4);
+    p->ws_bytes = off;
+    return MOE_OK;
+}
+
+// non-empty arrays must be non-null and 16-byte aligned
+static bool ptr_ok(const void *ptr, size_t nbytes)
+{
+    if (nbytes == 0) return true;
+    return ptr && (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0;
+}
+
+static bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (!na || !nb || !a || !b) return false;
+    const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+static moe_status check_qmat(const moe_qmat &m, const char *name, int64_t rows, int cols, int G)
+{
+    if (!ptr_ok(m.q, (size_t)rows * cols / 2) || !ptr_ok(m.s, (size_t)rows * (cols / G) * 2) ||
+        !ptr_ok(m.b, (size_t)rows * (cols / G) * 2))
+        return fail(MOE_ERR_ARG, "weight %s: null or misaligned pointer", name);
+    return MOE_OK;
+}
+
+static moe_status check_weights(const Plan &p, const moe_weights *w)
+{
+    if (!w) return fail(MOE_ERR_ARG, "weights struct is NULL");
+    moe_status st;
+    if ((st = check_qmat(w->gate, "gate", (int64_t)p.E * p.F, p.d, p.G))) return st;
+    if ((st = check_qmat(w->up, "up", (int64_t)p.E * p.F, p.d, p.G))) return st;
+    if ((st = check_qmat(w->down, "down", (int64_t)p.E * p.d, p.F, p.G))) return st;
+    if ((st = check_qmat(w->sgate, "sgate", p.Fs, p.d, p.G))) return st;
+    if ((st = check_qmat(w->sup, "sup", p.Fs, p.d, p.G))) return st;
+    if ((st = check_qmat(w->sdown, "sdown", p.d, p.Fs, p.G))) return st;
+    return MOE_OK;
+}
+
+static moe_status check_routing(const Plan &p, const moe_routing *r)
+{
+    if (!r) return fail(MOE_ERR_ARG, "routing struct is NULL");
+    const size_t A4 = (size_t)p.A * 4, MT4 = (size_t)p.max_tiles * 4;
+    if (!ptr_ok(r->topk_ids, A4) || !ptr_ok(r->topk_w, A4) || !ptr_ok(r->counts, (size_t)p.E * 4) ||
+        !ptr_ok(r->offsets, (size_t)(p.E + 1) * 4) || !ptr_ok(r->perm, A4) || !ptr_ok(r->inv_perm, A4) ||
+        !ptr_ok(r->tile_expert, MT4) || !ptr_ok(r->tile_row0, MT4) || !ptr_ok(r->tile_rows, MT4) ||
+        !ptr_ok(r->num_tiles, 4))
+        return fail(MOE_ERR_ARG, "routing: null or misaligned pointer");
+    return MOE_OK;
+}
+
+static moe_status common(const moe_dims *dims, Plan *p, void *ws, size_t ws_bytes)
+{
+    const char *why = "";
+    moe_status st = make_plan(dims, p, &why);
+    if (st != MOE_OK) return fail(st, "%s", why);
+    if (ws_bytes < p->ws_bytes)
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p->ws_bytes);
+    if (!ptr_ok(ws, p->ws_bytes)) return fail(MOE_ERR_ARG, "workspace: null or misaligned pointer");
+    return MOE_OK;
+}
+
+static moe_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+MOE_API int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_API int32_t moe_tile_m(const moe_dims *dims)
+{
+    Plan p;
+    const char *why;
+    return make_plan(dims, &p, &why) == MOE_OK ? p.tile_m : 0;
+}
+
+MOE_API size_t moe_max_tiles(const moe_dims *dims)
+{
+    Plan p;
+    const char *why;
+    return make_plan(dims, &p, &why) == MOE_OK ? (size_t)p.max_tiles : 0;
+}
+
+MOE_API size_t moe_workspace_bytes(const moe_dims *dims)
+{
+    Plan p;
+    const char *why;
+    return make_plan(dims, &p, &why) == MOE_OK ? p.ws_bytes : 0;
+}
+
+MOE_API moe_status moe_route(const moe_dims *dims, const float *logits, const moe_routing *out,
+                             void *ws, size_t ws_bytes, void *stream)
+{
+    Plan p;
+    moe_status st = common(dims, &p, ws, ws_bytes);
+    if (st) return st;
+    if (!ptr_ok(logits, (size_t)p.T * p.E * 4)) return fail(MOE_ERR_ARG, "logits: null or misaligned pointer");
+    if ((st = check_routing(p, out))) return st;
+    (void)hipGetLastError();
+    return hip_status(launch_route(p, logits, *out, ws, (hipStream_t)stream), "moe_route launch");
+}
+
+MOE_API moe_status moe_ffn(const moe_dims *dims, const uint16_t *x, const moe_weights *w,
+                           const moe_routing *r, uint16_t *y, void *ws, size_t ws_bytes, void *stream)
+{
+    Plan p;
+    moe_status st = common(dims, &p, ws, ws_bytes);
+    if (st) return st;
+    const size_t xb = (size_t)p.T * p.d * 2;
+    if (!ptr_ok(x, xb) || !ptr_ok(y, xb)) return fail(MOE_ERR_ARG, "x / y: null or misaligned pointer");
+    if (overlap(x, xb, y, xb)) return fail(MOE_ERR_ARG, "x and y overlap");
+    if ((st = check_weights(p, w)) || (st = check_routing(p, r))) return st;
+    if (p.T == 0) return MOE_OK;
+    (void)hipGetLastError();
+    hipError_t e = (p.T == 1) ? launch_decode(p, nullptr, x, *w, *r, y, ws, (hipStream_t)stream)
+                              : launch_ffn_gemm(p, x, *w, *r, y, ws, (hipStream_t)stream);
+    return hip_status(e, "moe_ffn launch");
+}
+
+static int layer_kernels(const Plan &p)
+{
+    if (p.T == 1) return 2;              // decode gate/up, decode down
+    if (p.T == 0) return 1;              // route scan only
+    return 3 + 3;                        // route topk, scan, scatter; gate/up, down, combine
+}
+
+static moe_status layer_impl(const moe_dims *dims, const float *logits, const uint16_t *x,
+                             const moe_weights *w, const moe_routing *out, uint16_t *y, void *ws,
+                             size_t ws_bytes, void *stream, EventTrace *tr)
+{
+    Plan p;
+    moe_status st = common(dims, &p, ws, ws_bytes);
+    if (st) return st;
+    const size_t xb = (size_t)p.T * p.d * 2;
+    if (!ptr_ok(logits, (size_t)p.T * p.E * 4)) return fail(MOE_ERR_ARG, "logits: null or misaligned pointer");
+    if (!ptr_ok(x, xb) || !ptr_ok(y, xb)) return fail(MOE_ERR_ARG, "x / y: null or misaligned pointer");
+    if (overlap(x, xb, y, xb)) return fail(MOE_ERR_ARG, "x and y overlap");
+    if ((st = check_weights(p, w)) || (st = check_routing(p, out))) return st;
+    if (tr && tr->n < 2 * layer_kernels(p))
+        return fail(MOE_ERR_ARG, "need %d events, got %d", 2 * layer_kernels(p), tr->n);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    hipError_t e;
+    if (p.T == 1) {
+        e = launch_decode(p, logits, x, *w, *out, y, ws, s, tr);
+    } else {
+        e = launch_route(p, logits, *out, ws, s, tr);
+        if (e == hipSuccess && p.T > 0) e = launch_ffn_gemm(p, x, *w, *out, y, ws, s, tr);
+    }
+    return hip_status(e, "moe_layer launch");
+}
+
+MOE_API moe_status moe_layer(const moe_dims *dims, const float *logits, const uint16_t *x,
+                             const moe_weights *w, const moe_routing *out, uint16_t *y, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    return layer_impl(dims, logits, x, w, out, y, ws, ws_bytes, stream, nullptr);
+}
+
+MOE_API int32_t moe_layer_kernels(const moe_dims *dims)
+{
+    Plan p;
+    const char *why;
+    return make_plan(dims, &p, &why) == MOE_OK ? layer_kernels(p) : 0;
+}
+
+MOE_API moe_status moe_layer_timed(const moe_dims *dims, const float *logits, const uint16_t *x,
+                                   const moe_weights *w, const moe_routing *out, uint16_t *y,
+                                   void *ws, size_t ws_bytes, void *stream, void *const *events,
+                                   int32_t n_events)
+{
+    if (!events) return fail(MOE_ERR_ARG, "events is NULL");
+    EventTrace tr;
+    tr.ev = reinterpret_cast<hipEvent_t *>(const_cast<void **>(events));
+    tr.n = n_events;
+    return layer_impl(dims, logits, x, w, out, y, ws, ws_bytes, stream, &tr);
+}
+
+MOE_API moe_status moe_dequant(const moe_qmat *m, int32_t rows, int32_t cols, int32_t G,
+                               uint16_t *out_bf16, void *stream)
+{
+    if (!m) return fail(MOE_ERR_ARG, "qmat is NULL");
+    if (G != 32 && G != 64 && G != 128) return fail(MOE_ERR_SHAPE, "G not in {32, 64, 128}");
+    if (rows < 0 || cols <= 0 || cols % 32 || cols % G) return fail(MOE_ERR_SHAPE, "bad rows / cols");
+    const size_t n = (size_t)rows * cols;
+    if (!ptr_ok(m->q, n / 2) || !ptr_ok(m->s, n / G * 2) || !ptr_ok(m->b, n / G * 2) ||
+        !ptr_ok(out_bf16, n * 2))
+        return fail(MOE_ERR_ARG, "null or misaligned pointer");
+    (void)hipGetLastError();
+    return hip_status(launch_dequant(*m, rows, cols, G, out_bf16, (hipStream_t)stream), "moe_dequant launch");
+}
+
+MOE_API const char *moe_status_string(moe_status s)
+{
+    switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_SHAPE: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+MOE_API const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

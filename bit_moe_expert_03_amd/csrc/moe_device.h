@@ -1,0 +1,182 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer:
+// bf16 conversion, the 4-bit affine decode, wave-wide reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
+{
+    return __uint_as_float(bits16 << 16);
+}
+
+// byte i of v as fp32 (v_cvt_f32_ubyte{0..3})
+template <int I>
+__device__ __forceinline__ float ubyte_f32(uint32_t v)
+{
+    return (float)((v >> (8 * I)) & 0xFFu);
+}
+
+// two fp32 -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32);
+// `lo` lands in bits 0..15
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu);
+}
+
+// Decode 8 consecutive 4-bit codes (one dword; element 2m in the low nibble
+// of byte m) of one affine group to 4 packed bf16 pairs, element 2r in the
+// low half of out[r].  Value = bf16_rne(fma(s, q, b)); s*q is exact in fp32,
+// so the fma rounds the exact s*q + b once.
+__device__ __forceinline__ void dequant8_bf16(uint32_t v, float s, float b, uint32_t out[4])
+{
+    const uint32_t lo = v & 0x0F0F0F0Fu;         // elements 0,2,4,6
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;  // elements 1,3,5,7
+    out[0] = pack_bf16x2(__builtin_fmaf(s, ubyte_f32<0>(lo), b),
+                         __builtin_fmaf(s, ubyte_f32<0>(hi), b));
+    out[1] = pack_bf16x2(__builtin_fmaf(s, ubyte_f32<1>(lo), b),
+                         __builtin_fmaf(s, ubyte_f32<1>(hi), b));
+    out[2] = pack_bf16x2(__builtin_fmaf(s, ubyte_f32<2>(lo), b),
+                         __builtin_fmaf(s, ubyte_f32<2>(hi), b));
+    out[3] = pack_bf16x2(__builtin_fmaf(s, ubyte_f32<3>(lo), b),
+                         __builtin_fmaf(s, ubyte_f32<3>(hi), b));
+}
+
+// sum_i q_i * x_i over the 8 codes of one dword (x in element order)
+__device__ __forceinline__ float dot8_codes(uint32_t v, const float *x, float acc)
+{
+    const uint32_t lo = v & 0x0F0F0F0Fu;
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+    acc = __builtin_fmaf(ubyte_f32<0>(lo), x[0], acc);
+    acc = __builtin_fmaf(ubyte_f32<0>(hi), x[1], acc);
+    acc = __builtin_fmaf(ubyte_f32<1>(lo), x[2], acc);
+    acc = __builtin_fmaf(ubyte_f32<1>(hi), x[3], acc);
+    acc = __builtin_fmaf(ubyte_f32<2>(lo), x[4], acc);
+    acc = __builtin_fmaf(ubyte_f32<2>(hi), x[5], acc);
+    acc = __builtin_fmaf(ubyte_f32<3>(lo), x[6], acc);
+    acc = __builtin_fmaf(ubyte_f32<3>(hi), x[7], acc);
+    return acc;
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
+}
+
+// sum over the 64 lanes, broadcast to all: butterflies inside rows of 16
+// (quad permutes, row rotates), then row broadcasts 15 and 31 into lane 63
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp_f32<0xB1>(v);         // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);         // quad_perm [2,3,0,1]
+    v += dpp_f32<0x124>(v);        // row_ror:4
+    v += dpp_f32<0x128>(v);        // row_ror:8  -> every lane holds its row sum
+    v += dpp_f32<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_f32<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Total order on finite fp32 logits as unsigned keys: larger logit -> larger
+// key; -0 is folded into +0 first so that the two compare equal.
+__device__ __forceinline__ uint32_t logit_key(float l)
+{
+    uint32_t u = (l == 0.0f) ? 0u : __float_as_uint(l);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_logit(uint32_t k)
+{
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+// DPP move of v within rows of 16 lanes / across rows; lanes with no source
+// get 0, the identity of an unsigned max.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+}
+
+// max over the 64 lanes, broadcast to all (DPP row shifts, then row
+// broadcasts 15 and 31 carry the row maxima to lane 63)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<0x111>(v));        // row_shr:1
+    v = max(v, dpp_u32<0x112>(v));        // row_shr:2
+    v = max(v, dpp_u32<0x114>(v));        // row_shr:4
+    v = max(v, dpp_u32<0x118>(v));        // row_shr:8
+    v = max(v, dpp_u32<0x142, 0xA>(v));   // row_bcast:15 into rows 1 and 3
+    v = max(v, dpp_u32<0x143, 0xC>(v));   // row_bcast:31 into rows 2 and 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top-k of one row of E <= 256 logits by one wave.  Lane l holds experts
+// 4l .. 4l+3, so among lanes holding the largest key the lowest lane holds
+// the lowest id.  Each round: wave max of the ordered keys (DPP), the lowest
+// lane and slot holding it (ballot, find-first), clear that slot.  Selected
+// (id, logit) of round j end up in lane j % 64, register j / 64.
+struct TopK {
+    int id[4];
+    float logit[4];
+    float lmax;
+};
+
+__device__ __forceinline__ void wave_topk(const float *__restrict__ L, int E, int k, TopK &out)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t key[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int e = 4 * lane + c;
+        key[c] = (e < E) ? logit_key(L[e]) : 0u;  // 0: no expert (finite keys are > 0)
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) { out.id[c] = 0; out.logit[c] = 0.f; }
+    out.lmax = 0.f;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t local = max(max(key[0], key[1]), max(key[2], key[3]));
+        const uint32_t m = wave_max_u32(local);
+        const uint64_t holders = __ballot(local == m);
+        const int wl = __ffsll((unsigned long long)holders) - 1;  // lowest lane with the max
+        int slot = 3;
+#pragma unroll
+        for (int c = 2; c >= 0; --c)
+            if (key[c] == m) slot = c;
+        slot = __builtin_amdgcn_readlane(slot, wl);
+        if (lane == wl) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (c == slot) key[c] = 0u;
+        }
+        const float l = key_logit(m);
+        if (j == 0) out.lmax = l;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (j == lane + 64 * c) { out.id[c] = 4 * wl + slot; out.logit[c] = l; }
+    }
+}
+
+__device__ __forceinline__ float silu(float z)
+{
+    return z / (1.0f + __expf(-z));
+}
+
+}  // namespace moe

@@ -1,0 +1,79 @@
+// Host-side internals of the MoE library: derived launch geometry, workspace
+// carving and the kernel launchers each .hip file provides.
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kRouteThreads = 1024;  // routing kernels: 16 waves per block
+constexpr int kRouteMaxBlocks = 512; // cap on route blocks (bounds the scan's input)
+constexpr int kMaxE = 256;
+
+// Everything derived from moe_dims that the launchers need.
+struct Plan {
+    int T, d, E, k, F, Fs, G, tile_m;
+    int64_t A;          // assignments T*k
+    int route_tb;       // tokens per route block
+    int route_nb;       // route blocks
+    int64_t max_tiles;  // length of the tile arrays
+    // workspace carving (byte offsets)
+    size_t off_hist, off_hr, off_hs, off_obuf, off_dech, ws_bytes;
+};
+
+// Optional per-kernel timing (measurement entry point): kernel i of a call
+// is launched with events[2i] / events[2i+1] as the start / stop events of
+// hipExtLaunchKernel, which time exactly that dispatch on its stream.
+struct EventTrace {
+    hipEvent_t *ev = nullptr;
+    int n = 0, i = 0;
+    bool take(hipEvent_t *start, hipEvent_t *stop)
+    {
+        if (!ev || i + 1 >= n) return false;
+        *start = ev[i];
+        *stop = ev[i + 1];
+        i += 2;
+        return true;
+    }
+};
+
+// launch `kernel`, timed by the next event pair of `tr` if there is one
+template <typename... KArgs, typename... Args>
+inline void launch(EventTrace *tr, void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem,
+                   hipStream_t s, Args... args)
+{
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (tr && tr->take(&e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
+
+// Fills *p; returns MOE_OK or MOE_ERR_SHAPE with a message in *why.
+moe_status make_plan(const moe_dims *dims, Plan *p, const char **why);
+
+// ---- route.hip
+hipError_t launch_route(const Plan &p, const float *logits, const moe_routing &r, void *ws,
+                        hipStream_t s, EventTrace *tr = nullptr);
+
+// ---- gemm.hip (T >= 2 path)
+hipError_t launch_ffn_gemm(const Plan &p, const uint16_t *x, const moe_weights &w,
+                           const moe_routing &r, uint16_t *y, void *ws, hipStream_t s,
+                           EventTrace *tr = nullptr);
+
+// ---- decode.hip (T == 1 path); when logits != nullptr the routing is
+// computed in-kernel and written to r, else it is read from r.
+hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
+                         const moe_weights &w, const moe_routing &r, uint16_t *y, void *ws,
+                         hipStream_t s, EventTrace *tr = nullptr);
+
+// ---- dequant.hip
+hipError_t launch_dequant(const moe_qmat &m, int rows, int cols, int G, uint16_t *out,
+                          hipStream_t s);
+
+}  // namespace moe

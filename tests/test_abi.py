@@ -1,0 +1,111 @@
+"""C ABI on the CPU: the library loads, exports every function include/moe.h
+declares, and its host-only calls (sizes, validation) behave -- no kernel is
+launched here (every error below is caught before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_moe_expert_03_amd import binding as B
+from bit_moe_expert_03_amd import workload as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+
+
+def test_header_lists_the_binding_exports():
+    assert sorted(header_functions()) == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+    assert B.moe_abi_version() == 1
+
+
+def test_status_strings():
+    L = B.lib()
+    for st in range(5):
+        assert L.moe_status_string(st)
+
+
+@pytest.mark.parametrize("name", list(wl.CONFIGS))
+def test_sizes_of_the_workloads(name):
+    dm = B.make_dims(wl.CONFIGS[name])
+    tm = B.moe_tile_m(dm)
+    assert tm in (32, 64, 128)
+    A = dm.T * dm.k
+    assert B.moe_max_tiles(dm) == -(-A // tm) + min(dm.E, A)
+    ws = B.moe_workspace_bytes(dm)
+    # the workspace holds at least h (routed + shared) and the routed outputs
+    assert ws >= A * dm.F * 2 + dm.T * dm.Fs * 2 + A * dm.d * 2
+
+
+def test_explicit_tile_m_is_kept():
+    for tm in (32, 64, 128):
+        dm = B.make_dims(wl.CONFIGS["c2_prefill512"], tile_m=tm)
+        assert B.moe_tile_m(dm) == tm
+
+
+BAD = [
+    dict(E=0), dict(E=257), dict(k=0), dict(k=17), dict(G=16), dict(d=96), dict(F=100),
+    dict(Fs=0), dict(T=-1), dict(tile_m=48), dict(d=64 * 300),
+]
+
+
+@pytest.mark.parametrize("bad", BAD, ids=[str(b) for b in BAD])
+def test_invalid_dims_are_rejected_without_launch(bad):
+    base = dict(T=16, d=256, E=16, k=2, F=128, Fs=128, G=32, tile_m=0)
+    base.update(bad)
+    dm = B.moe_dims(**base)
+    assert B.moe_tile_m(dm) == 0 and B.moe_max_tiles(dm) == 0 and B.moe_workspace_bytes(dm) == 0
+    r = B.moe_routing()
+    st = B.lib().moe_route(ctypes.byref(dm), None, ctypes.byref(r), None, 0, None)
+    assert st == B.MOE_ERR_SHAPE
+    assert B.lib().moe_last_error()
+
+
+def _fake_ptr(i):
+    # distinct aligned non-null host addresses: never dereferenced, since every
+    # call below fails validation before anything is launched
+    return 0x10000000 + 0x100000 * i
+
+
+def test_null_pointers_and_small_workspace_are_rejected():
+    L = B.lib()
+    dm = B.make_dims(wl.CONFIGS["c0_tiny"])
+    need = B.moe_workspace_bytes(dm)
+    r = B.moe_routing(*[_fake_ptr(i) for i in range(10)])
+    # workspace too small
+    st = L.moe_route(ctypes.byref(dm), _fake_ptr(20), ctypes.byref(r), _fake_ptr(21), need - 1, None)
+    assert st == B.MOE_ERR_WORKSPACE
+    # null logits
+    st = L.moe_route(ctypes.byref(dm), None, ctypes.byref(r), _fake_ptr(21), need, None)
+    assert st == B.MOE_ERR_ARG
+    # misaligned routing pointer
+    r2 = B.moe_routing(*[_fake_ptr(i) for i in range(10)])
+    r2.perm = _fake_ptr(4) + 4
+    st = L.moe_route(ctypes.byref(dm), _fake_ptr(20), ctypes.byref(r2), _fake_ptr(21), need, None)
+    assert st == B.MOE_ERR_ARG
+    # ffn: null weight pointer, x/y overlap
+    w = B.moe_weights(*[B.moe_qmat(_fake_ptr(30 + 3 * i), _fake_ptr(31 + 3 * i), _fake_ptr(32 + 3 * i))
+                        for i in range(6)])
+    w.down.q = None
+    st = L.moe_ffn(ctypes.byref(dm), _fake_ptr(50), ctypes.byref(w), ctypes.byref(r), _fake_ptr(51),
+                   _fake_ptr(21), need, None)
+    assert st == B.MOE_ERR_ARG and b"down" in L.moe_last_error()
+    w.down.q = _fake_ptr(36)
+    st = L.moe_ffn(ctypes.byref(dm), _fake_ptr(50), ctypes.byref(w), ctypes.byref(r), _fake_ptr(50) + 256,
+                   _fake_ptr(21), need, None)
+    assert st == B.MOE_ERR_ARG and b"overlap" in L.moe_last_error()
+    # dequant: bad G, bad cols
+    q = B.moe_qmat(_fake_ptr(60), _fake_ptr(61), _fake_ptr(62))
+    assert L.moe_dequant(ctypes.byref(q), 4, 64, 48, _fake_ptr(63), None) == B.MOE_ERR_SHAPE
+    assert L.moe_dequant(ctypes.byref(q), 4, 48, 32, _fake_ptr(63), None) == B.MOE_ERR_SHAPE

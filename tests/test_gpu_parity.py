@@ -1,0 +1,260 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Routing outputs and dequantised weights: bit-exact.  Routing weights: within
+1e-6 of the oracle's fp64 softmax and summing to 1 within 1e-6.  Layer output
+y (bf16): max|y - y_ref| <= 1e-2 max|y_ref| + 1e-3 against the fp64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_moe_expert_03_amd import binding as B
+from bit_moe_expert_03_amd import workload as wl
+from gpu_util import (bf16_to_f64, check_routing, check_y, dev, host_u16, run, sample_tokens,
+                      weights_to_dev)
+
+pytestmark = pytest.mark.gpu
+
+# shapes the oracle finishes in seconds that span several tiles and ragged tails
+SMALL = {
+    "ragged_T37_E16_k4": (wl.Dims(T=37, d=128, E=16, k=4, F=64, Fs=128, G=32), False),
+    "T300_E16_k4_G64": (wl.Dims(T=300, d=256, E=16, k=4, F=128, Fs=128, G=64), False),
+    "T70_E8_k3_G128": (wl.Dims(T=70, d=256, E=8, k=3, F=128, Fs=128, G=128), False),
+    "k_equals_E": (wl.Dims(T=9, d=64, E=4, k=4, F=64, Fs=64, G=32), False),
+    "E1_k1": (wl.Dims(T=33, d=64, E=1, k=1, F=64, Fs=64, G=64), False),
+    "T2_smallest_gemm": (wl.Dims(T=2, d=128, E=8, k=2, F=64, Fs=64, G=32), False),
+    "zipf_T500_E64_k6": (wl.Dims(T=500, d=128, E=64, k=6, F=64, Fs=64, G=32), True),
+    "T1_small_decode": (wl.Dims(T=1, d=256, E=16, k=4, F=128, Fs=192, G=64), False),
+}
+
+
+@pytest.fixture(scope="module")
+def cases():
+    return {}
+
+
+def _case(name):
+    if name in wl.CONFIGS:
+        return wl.make_case(name)
+    dims, zipf = SMALL[name]
+    return wl.make_case(dims, seed=100 + list(SMALL).index(name), zipf=zipf)
+
+
+# ------------------------------------------------------------------ dequant
+
+def test_dequant_bit_exact():
+    rng = np.random.default_rng(1)
+    for rows, cols, G in ((64, 256, 32), (512, 2048, 64), (96, 512, 128)):
+        q = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+        s = wl.to_bf16_bits(rng.uniform(-2, 2, (rows, cols // G)).astype(np.float32))
+        b = wl.to_bf16_bits(rng.uniform(-30, 30, (rows, cols // G)).astype(np.float32))
+        out = torch.empty((rows, cols), dtype=torch.int16, device="cuda")
+        B.moe_dequant(dev(q), dev(s), dev(b), rows, cols, G, out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_u16(out), oracle.dequant_bf16(q, s, b, rows, cols, G))
+
+
+def test_dequant_workload_weights_bit_exact():
+    c = wl.make_case("c2_prefill512")
+    d = c["dims"]
+    for m, (rows, cols) in (("gate", (d.F, d.d)), ("down", (d.d, d.F))):
+        q, s, b = (c["w"][m][f][3] for f in ("q", "s", "b"))  # expert 3
+        out = torch.empty((rows, cols), dtype=torch.int16, device="cuda")
+        B.moe_dequant(dev(q), dev(s), dev(b), rows, cols, d.G, out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_u16(out), oracle.dequant_bf16(q, s, b, rows, cols, d.G))
+
+
+# ------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("name", list(wl.CONFIGS))
+def test_route_bit_exact_workloads(name):
+    c = wl.make_case(name, weights=False)
+    dm = B.make_dims(c["dims"])
+    r = B.alloc_routing(dm)
+    ws = B.alloc_workspace(dm)
+    B.moe_route(dm, dev(c["logits"]), r, ws)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in r.items()}
+    g["tile_m"], g["max_tiles"] = B.moe_tile_m(dm), B.moe_max_tiles(dm)
+    check_routing(c, g)
+
+
+@pytest.mark.parametrize("tile_m", [32, 64, 128])
+def test_route_tie_heavy_and_signed_zero(tile_m):
+    rng = np.random.default_rng(tile_m)
+    dims = wl.Dims(T=777, d=64, E=256, k=8, F=64, Fs=64, G=32)
+    L = rng.integers(-2, 3, (dims.T, dims.E)).astype(np.float32)
+    L[::3] *= 0.0  # rows of signed zeros: -0.0 and +0.0 must tie
+    L[1::3] = np.where(rng.random((len(L[1::3]), dims.E)) < 0.5, -0.0, L[1::3])
+    c = {"dims": dims, "logits": L}
+    dm = B.make_dims(dims, tile_m)
+    r = B.alloc_routing(dm)
+    B.moe_route(dm, dev(L), r, B.alloc_workspace(dm))
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in r.items()}
+    g["tile_m"], g["max_tiles"] = tile_m, B.moe_max_tiles(dm)
+    check_routing(c, g)
+
+
+def test_route_empty_batch():
+    dims = wl.Dims(T=0, d=64, E=8, k=2, F=64, Fs=64, G=32)
+    dm = B.make_dims(dims)
+    r = B.alloc_routing(dm)
+    for t in r.values():
+        t.fill_(-7)
+    B.moe_route(dm, torch.empty((0, 8), device="cuda"), r, B.alloc_workspace(dm))
+    torch.cuda.synchronize()
+    assert np.all(r["counts"].cpu().numpy() == 0)
+    assert np.all(r["offsets"].cpu().numpy() == 0)
+    assert int(r["num_tiles"].cpu()[0]) == 0
+
+
+# ------------------------------------------------------------------ layer
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small_shapes_all_tokens(name):
+    c = _case(name)
+    for mode in ("layer", "split"):
+        g = run(c, mode=mode)
+        ref = check_routing(c, g)
+        check_y(c, g, ref)
+
+
+def test_layer_tiny_config_all_tokens():
+    c = wl.make_case("c0_tiny")
+    for tile_m in (0, 32, 64, 128):
+        g = run(c, tile_m=tile_m)
+        ref = check_routing(c, g)
+        check_y(c, g, ref)
+
+
+@pytest.mark.parametrize("tile_m", [0, 32, 128])
+def test_layer_prefill512_sampled(tile_m):
+    c = wl.make_case("c2_prefill512")
+    g = run(c, tile_m=tile_m, mode="split" if tile_m == 32 else "layer")
+    ref = check_routing(c, g)
+    check_y(c, g, ref, tokens=sample_tokens(c, ref, n_random=48))
+
+
+@pytest.mark.parametrize("name", ["c3_prefill4096_zipf", "c4_prefill32768"])
+def test_layer_full_size_sampled(name):
+    c = wl.make_case(name)
+    g = run(c)
+    ref = check_routing(c, g)
+    check_y(c, g, ref, tokens=sample_tokens(c, ref))
+
+
+@pytest.mark.parametrize("index", [0, 1])
+def test_decode_full_size(index):
+    c = wl.make_case("c1_decode", index=index)
+    for mode in ("layer", "split"):
+        g = run(c, mode=mode)
+        ref = check_routing(c, g)
+        check_y(c, g, ref)
+
+
+# ------------------------------------------------------------------ properties
+
+@pytest.mark.parametrize("name", ["c0_tiny", "c1_decode", "T300_E16_k4_G64"])
+def test_deterministic(name):
+    c = _case(name)
+    wdev = weights_to_dev(c["w"])
+    a = run(c, wdev=wdev)
+    b = run(c, wdev=wdev)
+    for k in ("topk_ids", "topk_w", "perm", "y_bits"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+@pytest.mark.parametrize("name", ["c0_tiny", "c1_decode", "T300_E16_k4_G64"])
+def test_doubling_down_scales_doubles_y(name):
+    c = _case(name)
+    g = run(c)
+    c2 = dict(c)
+    c2["w"] = {m: dict(v) for m, v in c["w"].items()}
+    for m in ("down", "sdown"):
+        for f in ("s", "b"):
+            c2["w"][m][f] = wl.to_bf16_bits(2.0 * bf16_to_f64(c["w"][m][f]).astype(np.float32))
+    g2 = run(c2)
+    np.testing.assert_array_equal(g2["y"], 2.0 * g["y"])
+
+
+def test_token_permutation_permutes_rows():
+    c = _case("T300_E16_k4_G64")
+    g = run(c)
+    p = np.random.default_rng(0).permutation(c["dims"].T)
+    c2 = dict(c)
+    c2["x"] = np.ascontiguousarray(c["x"][p])
+    c2["logits"] = np.ascontiguousarray(c["logits"][p])
+    g2 = run(c2)
+    np.testing.assert_array_equal(g2["y_bits"], g["y_bits"][p])
+
+
+def test_expert_relabelling_leaves_y_unchanged():
+    c = _case("T300_E16_k4_G64")
+    g = run(c)
+    p = np.random.default_rng(1).permutation(c["dims"].E)
+    c2 = dict(c)
+    c2["w"] = {m: ({f: np.ascontiguousarray(a[p]) for f, a in v.items()} if m in ("gate", "up", "down") else v)
+               for m, v in c["w"].items()}
+    c2["logits"] = np.ascontiguousarray(c["logits"][:, p])
+    g2 = run(c2)
+    np.testing.assert_array_equal(g2["y_bits"], g["y_bits"])
+
+
+# ------------------------------------------------------------------ launch forms
+
+@pytest.mark.parametrize("name", ["c0_tiny", "T1_small_decode"])
+def test_timed_entry_point_matches_and_times(name):
+    c = _case(name)
+    dims = c["dims"]
+    dm = B.make_dims(dims)
+    g = run(c)
+    wdev = weights_to_dev(c["w"])
+    nk = B.moe_layer_kernels(dm)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    r = B.alloc_routing(dm)
+    y = torch.empty((dims.T, dims.d), dtype=torch.int16, device="cuda")
+    B.moe_layer_timed(dm, dev(c["logits"]), dev(c["x"]), wdev, r, y, B.alloc_workspace(dm),
+                      [e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u16(y), g["y_bits"])
+    times = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(nk)]
+    assert all(t > 0 for t in times), times
+    with pytest.raises(B.MoeError):  # too few events: rejected before any launch
+        B.moe_layer_timed(dm, dev(c["logits"]), dev(c["x"]), wdev, r, y, B.alloc_workspace(dm),
+                          [e.cuda_event for e in evs[:-1]])
+
+
+@pytest.mark.parametrize("name", ["c0_tiny", "T1_small_decode", "T300_E16_k4_G64"])
+def test_graph_replays_match_eager(name):
+    c = _case(name)
+    dims = c["dims"]
+    dm = B.make_dims(dims)
+    eager = run(c)
+    wdev = weights_to_dev(c["w"])
+    lg, x = dev(c["logits"]), dev(c["x"])
+    r = B.alloc_routing(dm)
+    ws = B.alloc_workspace(dm)
+    y = torch.empty((dims.T, dims.d), dtype=torch.int16, device="cuda")
+    s = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr, stream=s):
+            B.moe_layer(dm, lg, x, wdev, r, y, ws, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(0x7FC1)
+        r["perm"].fill_(-7)
+        gr.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_u16(y), eager["y_bits"], err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(r["perm"].cpu().numpy(), eager["perm"])
+        # the program's own eager work between replays
+        B.moe_layer(dm, lg, x, wdev, B.alloc_routing(dm), torch.empty_like(y), B.alloc_workspace(dm))
+        torch.cuda.synchronize()
