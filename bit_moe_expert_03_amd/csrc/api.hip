@@ -64,10 +64,11 @@ moe_status make_plan(const moe_dims *dm, Plan *p, const char **why)
     if (tb < 16) tb = 16;
     p->route_tb = tb;
     p->route_nb = (d.T + tb - 1) / tb;
+    p->route_nbp = (p->route_nb + 15) & ~15;
     p->max_tiles = (p->A + p->tile_m - 1) / p->tile_m + (p->A < d.E ? p->A : d.E);
     const int Fmax = d.F > d.Fs ? d.F : d.Fs;
     size_t off = 0;
-    p->off_hist = off; off = align_up(off + (size_t)d.E * p->route_nb * 4);
+    p->off_hist = off; off = align_up(off + (size_t)d.E * p->route_nbp * 4);
     p->off_hr = off;   off = align_up(off + (size_t)p->A * d.F * 2);
     p->off_hs = off;   off = align_up(off + (size_t)d.T * d.Fs * 2);
     p->off_obuf = off; off = align_up(off + (size_t)(p->A + d.T) * d.d * 2);

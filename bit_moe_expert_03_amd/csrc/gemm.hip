@@ -42,8 +42,6 @@ namespace moe {
 
 constexpr int kGemmThreads = 256;      // 4 waves
 constexpr int kKStep = 64;             // contraction per main-loop step
-constexpr int kLdsPitch = kKStep + 8;  // bf16 per LDS row (pad against bank conflicts)
-constexpr int kStages = 3;             // LDS ring depth for A
 
 struct GemmTiles {
     const int32_t *tile_expert, *tile_row0, *tile_rows, *num_tiles;
@@ -84,133 +82,329 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblk_pad)
     return (bid & 7) * per + (bid >> 3);
 }
 
-template <int BM>
-struct ATile {
-    static constexpr int kPer = BM * (kKStep / 8) / kGemmThreads;  // 16-byte chunks per thread
-    uint4 v[kPer];
-};
+// ---- LDS layout -----------------------------------------------------------
+// Every buffer below is its own LDS object, filled by global->LDS copies
+// (global_load_lds_dwordx4) and indexed statically, so the compiler can tell
+// a buffer being read from the one being filled and does not wait for
+// copies that are still in flight.
+// A stages (2): [MS*32 rows][64 bf16] (128-byte rows); the eight 16-byte
+// chunks of row r are stored XOR-permuted, chunk c at slot c ^ ((r >> 1) & 7),
+// which keeps the MFMA operand reads (16 rows x one chunk) free of bank
+// conflicts.
+// B buffers (2, one per pair of K steps): [4 waves][64 rows][64 bytes] of raw
+// 4-bit codes; chunk c of row r at slot c ^ ((r >> 2) & 3).
+constexpr int kMaxMS = 4;
+constexpr int kARow = 128;                        // bytes per A row in LDS
+constexpr int kBRow = 64;                         // bytes of codes per B row per pair of K steps
+constexpr int kBWave = 64 * kBRow;                // 4 KB per wave
+constexpr int kBBuf = 4 * kBWave;                 // 16 KB per buffer
 
-template <int BM>
-__device__ __forceinline__ void a_load(ATile<BM> &t, const uint16_t *const (&rowp)[ATile<BM>::kPer],
-                                       int kcol0)
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
 {
-    const int chunk = threadIdx.x & 7;
-#pragma unroll
-    for (int i = 0; i < ATile<BM>::kPer; ++i)
-        t.v[i] = rowp[i] ? *reinterpret_cast<const uint4 *>(rowp[i] + kcol0 + chunk * 8)
-                         : make_uint4(0, 0, 0, 0);
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-template <int BM>
-__device__ __forceinline__ void a_store(const ATile<BM> &t, uint16_t *lds)
+// Workgroup barrier without a memory fence: a fence would also wait for the
+// global->LDS copies of later steps; every wave waits for its own copies of
+// the current step (wait_vmcnt) before arriving, so after the barrier the
+// whole step is in LDS.
+__device__ __forceinline__ void block_sync()
 {
-    const int chunk = threadIdx.x & 7;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
+// Copy the A tile of K step kt (MS*32 rows x 64 bf16) into an A stage:
+// wave w, copy i moves rows 8 (4 i + w) .. +7, 8 lanes per 128-byte row.
+// rowp[i] is this lane's source row of copy i (rows past the tile's end
+// point at a valid row; their products land in discarded output rows).
+template <int MS>
+__device__ __forceinline__ void a_dma(const uint16_t *const (&rowp)[MS], int kt, uint8_t *stage)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slot = lane & 7;
 #pragma unroll
-    for (int i = 0; i < ATile<BM>::kPer; ++i) {
-        const int row = (threadIdx.x >> 3) + i * (kGemmThreads / 8);
-        *reinterpret_cast<uint4 *>(lds + row * kLdsPitch + chunk * 8) = t.v[i];
+    for (int i = 0; i < MS; ++i) {
+        const int row = 8 * (4 * i + wave) + (lane >> 3);
+        const int c = slot ^ ((row >> 1) & 7);  // source chunk stored in this slot
+        __builtin_amdgcn_global_load_lds((const void *)(rowp[i] + kt * kKStep + c * 8),
+                                         (lds_void_t *)(stage + (4 * i + wave) * 1024), 16, 0, 0);
     }
 }
 
-// B operand source of one lane: a row of a packed matrix
-struct BRow {
-    const uint8_t *q;   // codes of the row
-    const uint16_t *s;  // scales of the row
-    const uint16_t *b;  // biases of the row
+// Per-wave B source: the 64 rows this wave multiplies (rows 0..31 feed the
+// first accumulator set, 32..63 the second) and their scale/bias rows.
+struct BSrc {
+    const uint8_t *q[4];   // code row of the 16-row group this lane copies in DMA step q
+    const uint16_t *s0, *b0, *s1, *b1;  // scale/bias rows of this lane's two MFMA columns
+    int kbytes;            // bytes of codes per row (K / 2)
+    int ngroups;           // groups per row (K / G)
 };
 
-struct BRaw {
-    uint4 q;
-    uint32_t sb;  // bf16 scale (low half), bf16 bias (high half)
-};
-
-__device__ __forceinline__ void b_load(BRaw &r, const BRow &row, int kstep, int half, int G)
+// Copy the codes of pair p (K steps 2p, 2p+1: 64 bytes per row) of this
+// wave's 64 rows into its slice of an LDS buffer: 4 copies of 16 rows x 64 B.
+__device__ __forceinline__ void b_dma(const BSrc &src, int p, uint8_t *wave_buf)
 {
-    const int k0 = kstep * kKStep + 32 * half;
-    r.q = *reinterpret_cast<const uint4 *>(row.q + (k0 >> 1));
-    const int g = k0 / G;
-    r.sb = (uint32_t)row.s[g] | ((uint32_t)row.b[g] << 16);
+    const int lane = threadIdx.x & 63;
+    const int sub = lane >> 2;          // row within the 16-row group
+    const int slot = lane & 3;          // destination chunk slot
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = 16 * q + sub;
+        const int c = slot ^ ((r >> 2) & 3);  // source chunk stored in this slot
+        const int off = min(64 * p + 16 * c, src.kbytes - 16);
+        __builtin_amdgcn_global_load_lds((const void *)(src.q[q] + off), (lds_void_t *)(wave_buf + q * 1024), 16, 0,
+                                         0);
+    }
 }
 
-__device__ __forceinline__ void b_decode(const BRaw &r, bf16x8 op[4])
+// scale/bias words of one pair for the lane's two rows (NW words of two
+// bf16 each; group order = pair's groups in ascending order)
+template <int G>
+struct SBPair {
+    static constexpr int NW = G == 32 ? 2 : 1;
+    uint32_t s0[NW], b0[NW], s1[NW], b1[NW];
+};
+
+template <int G>
+__device__ __forceinline__ void sb_load(SBPair<G> &t, const BSrc &src, int p)
 {
-    const float s = __uint_as_float(r.sb << 16), b = __uint_as_float(r.sb & 0xFFFF0000u);
-    const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    constexpr int NG = 128 / G;  // groups per pair
+    const int g0 = p * NG;
+    if constexpr (G == 128) {
+        t.s0[0] = src.s0[g0]; t.b0[0] = src.b0[g0];
+        t.s1[0] = src.s1[g0]; t.b1[0] = src.b1[g0];
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t o[4];
-        dequant8_bf16(w[i], s, b, o);
-        op[i] = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+        for (int w = 0; w < SBPair<G>::NW; ++w) {
+            const int g = g0 + 2 * w;
+            if (g + 1 < src.ngroups) {  // both groups of the word exist: one 4-byte load
+                t.s0[w] = *reinterpret_cast<const uint32_t *>(src.s0 + g);
+                t.b0[w] = *reinterpret_cast<const uint32_t *>(src.b0 + g);
+                t.s1[w] = *reinterpret_cast<const uint32_t *>(src.s1 + g);
+                t.b1[w] = *reinterpret_cast<const uint32_t *>(src.b1 + g);
+            } else {  // tail of a row with an odd group count
+                const int gg = min(g, src.ngroups - 1);
+                t.s0[w] = src.s0[gg]; t.b0[w] = src.b0[gg];
+                t.s1[w] = src.s1[gg]; t.b1[w] = src.b1[gg];
+            }
+        }
     }
+}
+
+// scale (low 16 bits of the result) and bias of K step j of the pair, half h
+template <int G>
+__device__ __forceinline__ void sb_pick(const uint32_t (&s)[SBPair<G>::NW], const uint32_t (&b)[SBPair<G>::NW],
+                                        int j, int h, float &sf, float &bf)
+{
+    const int gi = (64 * j + 32 * h) / G;  // group index inside the pair
+    const uint32_t sw = s[gi >> 1 < SBPair<G>::NW ? gi >> 1 : 0];
+    const uint32_t bw = b[gi >> 1 < SBPair<G>::NW ? gi >> 1 : 0];
+    const int sh = (gi & 1) * 16;
+    sf = __uint_as_float((sw >> sh) << 16);
+    bf = __uint_as_float((bw >> sh) << 16);
+}
+
+__device__ __forceinline__ bf16x8 decode_sub(uint32_t w, float s, float b)
+{
+    uint32_t o[4];
+    dequant8_bf16(w, s, b, o);
+    return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// scheduling hint: interleave n MFMAs with the decode VALU and LDS reads of
+// the next sub-step (6 VALU ops fit under one 32x32x16 MFMA)
+template <int NMFMA, int NDS>
+__device__ __forceinline__ void interleave_hint()
+{
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
+    }
+}
+
+// One 64-wide K step: B codes of this lane from the wave's LDS buffer, A
+// operands from the A stage; the four 16-wide MFMA sub-steps are software
+// pipelined (decode and A reads of sub-step s+1 under the MFMAs of s).
+template <int MS, int G>
+__device__ __forceinline__ void kstep(const uint8_t *astage, const uint8_t *bwave, const SBPair<G> &sb, int j,
+                                      f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
+{
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, n = lane & 31;
+    const int c = 2 * j + h;  // code chunk of this step and half
+    const uint4 *bq = reinterpret_cast<const uint4 *>(__builtin_assume_aligned(bwave, 16));
+    const uint4 q0 = bq[n * (kBRow / 16) + (c ^ ((n >> 2) & 3))];
+    const int n1 = 32 + n;
+    const uint4 q1 = bq[n1 * (kBRow / 16) + (c ^ ((n1 >> 2) & 3))];
+    float s0, b0, s1, b1;
+    sb_pick<G>(sb.s0, sb.b0, j, h, s0, b0);
+    sb_pick<G>(sb.s1, sb.b1, j, h, s1, b1);
+    const uint32_t w0[4] = {q0.x, q0.y, q0.z, q0.w};
+    const uint32_t w1[4] = {q1.x, q1.y, q1.z, q1.w};
+    // A operand of sub-tile i, sub-step s: row 32 i + n, chunk 4 h + s
+    const bf16x8 *aq = reinterpret_cast<const bf16x8 *>(__builtin_assume_aligned(astage, 16));
+    auto aread = [&](int i, int s) __attribute__((always_inline)) {
+        const int row = 32 * i + n;
+        return aq[row * (kARow / 16) + ((4 * h + s) ^ ((row >> 1) & 7))];
+    };
+    bf16x8 o0[2], o1[2];
+    o0[0] = decode_sub(w0[0], s0, b0);
+    o1[0] = decode_sub(w1[0], s1, b1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int cu = s & 1, nx = cu ^ 1;
+        bf16x8 av[MS];
+#pragma unroll
+        for (int i = 0; i < MS; ++i) av[i] = aread(i, s);
+        if (s < 3) {
+            o0[nx] = decode_sub(w0[s + 1], s0, b0);
+            o1[nx] = decode_sub(w1[s + 1], s1, b1);
+        }
+#pragma unroll
+        for (int i = 0; i < MS; ++i) {
+            acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], o0[cu], acc0[i], 0, 0, 0);
+            acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], o1[cu], acc1[i], 0, 0, 0);
+        }
+        if (s < 3) interleave_hint<2 * MS, 0>();
+    }
+}
+
+// One K step of the main loop.  J = kt & 1 selects the A stage and the step
+// inside the pair, BUF the B buffer of the pair.  Entry: this wave's copies
+// of A(kt) (issued one step ago) and of the pair's codes (issued at the
+// previous pair's first step) must land: at odd steps the copies issued at
+// the pair's first step -- next pair's codes and scales, NB operations --
+// may stay in flight.
+template <int MS, int G, int J, int BUF>
+__device__ __forceinline__ void mainloop_step(int kt, int nk, int npair, const uint16_t *const (&rowp)[MS],
+                                              const BSrc &bsrc, uint8_t *a0, uint8_t *a1, uint8_t *b0,
+                                              uint8_t *b1, const SBPair<G> &sb, SBPair<G> &sbnext,
+                                              f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
+{
+    constexpr int NB = 4 + 4 * SBPair<G>::NW;  // copies + scale/bias loads of one pair
+    if constexpr (J == 1) wait_vmcnt<NB>(); else wait_vmcnt<0>();
+    block_sync();
+    a_dma<MS>(rowp, min(kt + 1, nk - 1), J == 0 ? a1 : a0);
+    if constexpr (J == 0) {
+        const int pn = min((kt >> 1) + 1, npair - 1);
+        b_dma(bsrc, pn, BUF == 0 ? b1 : b0);
+        sb_load<G>(sbnext, bsrc, pn);
+    }
+    kstep<MS, G>(J == 0 ? a0 : a1, BUF == 0 ? b0 : b1, sb, J, acc0, acc1);
 }
 
 // Main loop shared by both GEMMs: acc0 += A B0^T, acc1 += A B1^T over K for
-// the BM rows of the tile (32-row sub-tiles past `rows` are skipped).
-template <int BM>
-__device__ __forceinline__ void mainloop(const uint16_t *const (&rowp)[ATile<BM>::kPer], int K,
-                                         const BRow &b0, const BRow &b1, bool wave_active, int G,
-                                         int rows, uint16_t *lds, f32x16 (&acc0)[BM / 32],
-                                         f32x16 (&acc1)[BM / 32])
+// MS live 32-row sub-tiles.  Per K step: A of the next step and, at a
+// pair's first step, the codes and scales of the next pair are copied while
+// the MFMAs of this step run.  Past the end it re-loads valid steps instead
+// of branching; with K a multiple of 256 the 4-step body has no conditions.
+template <int MS, int G>
+__device__ __forceinline__ void mainloop(const uint16_t *const (&rowp)[MS], int K, const BSrc &bsrc,
+                                         uint8_t *lds_a0, uint8_t *lds_a1, uint8_t *lds_b0,
+                                         uint8_t *lds_b1, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
 {
-    constexpr int MS = BM / 32;
-    const int lane = threadIdx.x & 63;
-    const int half = lane >> 5, r32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint8_t *bw0 = lds_b0 + wave * kBWave;
+    uint8_t *bw1 = lds_b1 + wave * kBWave;
     const int nk = K / kKStep;
-    const int msub = (rows + 31) >> 5;  // sub-tiles with live rows (block-uniform)
+    const int npair = (nk + 1) >> 1;
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) { acc0[i][r] = 0.f; acc1[i][r] = 0.f; }
 
-    // prologue: A step 0 in LDS, A step 1 in registers, B steps 0 and 1 in registers
-    ATile<BM> at;
-    BRaw bq[2][2];
-    a_load<BM>(at, rowp, 0);
-    if (wave_active) {
-        b_load(bq[0][0], b0, 0, half, G);
-        b_load(bq[0][1], b1, 0, half, G);
-        if (nk > 1) { b_load(bq[1][0], b0, 1, half, G); b_load(bq[1][1], b1, 1, half, G); }
-    }
-    a_store<BM>(at, lds);
-    if (nk > 1) a_load<BM>(at, rowp, kKStep);
+    SBPair<G> sbc, sbn;
+    a_dma<MS>(rowp, 0, lds_a0);
+    b_dma(bsrc, 0, bw0);
+    sb_load<G>(sbc, bsrc, 0);
 
-    auto step = [&](int kt, BRaw (&cur)[2]) {
-        // stage the A tile of step kt+1 (loaded one step ago), fetch kt+2
-        if (kt + 1 < nk) a_store<BM>(at, lds + ((kt + 1) % kStages) * (BM * kLdsPitch));
-        if (kt + 2 < nk) a_load<BM>(at, rowp, (kt + 2) * kKStep);
-        __syncthreads();
-        if (!wave_active) return;
-        bf16x8 op0[4], op1[4];
-        b_decode(cur[0], op0);
-        b_decode(cur[1], op1);
-        if (kt + 2 < nk) { b_load(cur[0], b0, kt + 2, half, G); b_load(cur[1], b1, kt + 2, half, G); }
-        const uint16_t *buf = lds + (kt % kStages) * (BM * kLdsPitch);
+    int kt = 0;
+    for (; kt + 3 < nk; kt += 4) {  // pairs 2P (buffer 0) and 2P+1 (buffer 1)
+        mainloop_step<MS, G, 0, 0>(kt, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbc, sbn, acc0, acc1);
+        mainloop_step<MS, G, 1, 0>(kt + 1, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbc, sbn, acc0, acc1);
+        mainloop_step<MS, G, 0, 1>(kt + 2, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbn, sbc, acc0, acc1);
+        mainloop_step<MS, G, 1, 1>(kt + 3, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbn, sbc, acc0, acc1);
+    }
+    if (kt < nk) {  // 1 to 3 remaining steps (K not a multiple of 256)
+        mainloop_step<MS, G, 0, 0>(kt, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbc, sbn, acc0, acc1);
+        if (kt + 1 < nk)
+            mainloop_step<MS, G, 1, 0>(kt + 1, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbc, sbn, acc0, acc1);
+        if (kt + 2 < nk)
+            mainloop_step<MS, G, 0, 1>(kt + 2, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbn, sbc, acc0, acc1);
+    }
+    wait_vmcnt<0>();  // no copy into LDS outlives the loop
+}
+
+// gathered / contiguous A rows of one tile for sub-tiles < MS
+template <int MS>
+__device__ __forceinline__ void a_rows(const uint16_t *(&rowp)[MS], const uint16_t *base, int ld,
+                                       const int32_t *perm, int k, int row0, int rows)
+{
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int i = 0; i < MS; ++i) {
-                if (i < msub) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                        buf + (32 * i + r32) * kLdsPitch + 32 * half + 8 * s);
-                    acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op0[s], acc0[i], 0, 0, 0);
-                    acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op1[s], acc1[i], 0, 0, 0);
-                }
-            }
-        }
-    };
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, bq[0]);
-        if (kt + 1 < nk) step(kt + 1, bq[1]);
+    for (int i = 0; i < MS; ++i) {
+        const int m = min((int)(threadIdx.x >> 3) + i * (kGemmThreads / 8), rows - 1);
+        const int src = perm ? perm[row0 + m] / k : row0 + m;
+        rowp[i] = base + (size_t)src * ld;
     }
 }
 
-template <int BM>
+template <int MS, int G>
+__device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int rows, int N,
+                                            const moe_qmat &mg, const moe_qmat &mu, size_t ebase,
+                                            uint16_t *out, bool routed, int nt, uint8_t *lds_a0,
+                                            uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint16_t *rowp[MS];
+    a_rows<MS>(rowp, a.x, a.d, routed ? a.perm : nullptr, a.k, row0, rows);
+    const int ncol0 = nt * 128 + 32 * wave;  // first h column of this wave
+    const bool wave_active = ncol0 < N;
+    const int nbase = wave_active ? ncol0 : 0;
+    const int Kq = a.d >> 1, Kg = a.d / G;
+    BSrc src;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // DMA rows 16q + lane/4: q < 2 gate, q >= 2 up
+        const int r = 16 * q + (lane >> 2);
+        const moe_qmat &m = q < 2 ? mg : mu;
+        src.q[q] = m.q + (ebase + nbase + (r & 31)) * Kq;
+    }
+    const size_t brow = ebase + nbase + (lane & 31);
+    src.s0 = mg.s + brow * Kg; src.b0 = mg.b + brow * Kg;
+    src.s1 = mu.s + brow * Kg; src.b1 = mu.b + brow * Kg;
+    src.kbytes = Kq;
+    src.ngroups = Kg;
+    f32x16 accg[MS], accu[MS];
+    mainloop<MS, G>(rowp, a.d, src, lds_a0, lds_a1, lds_b0, lds_b1, accg, accu);
+    if (!wave_active) return;
+    const int half = lane >> 5;
+    const int n = nbase + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (m < rows)
+                out[(size_t)(row0 + m) * N + n] = f32_to_bf16(silu(accg[i][r]) * accu[i][r]);
+        }
+}
+
+template <int BM, int G>
 __global__ __launch_bounds__(kGemmThreads, 2) void moe_gateup_kernel(GateUpArgs a)
 {
-    constexpr int MS = BM / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * BM * kLdsPitch];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[BM * kARow];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[BM * kARow];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kBBuf];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kBBuf];
     const int L = xcd_logical_block(blockIdx.x, a.nblk_pad);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     int row0, rows, N, nt;
     const moe_qmat *mg, *mu;
     size_t ebase;  // first row of the expert's slab
@@ -239,46 +433,65 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gateup_kernel(GateUpArgs 
     } else {
         return;
     }
-    // gathered A rows owned by this thread for the global->LDS copy
-    const uint16_t *rowp[ATile<BM>::kPer];
+    const int msub = (rows + 31) >> 5;  // live 32-row sub-tiles (block-uniform)
+    if (BM >= 128 && msub > 2)
+        gateup_body<(BM >= 128 ? 4 : 1), G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+    else if (BM >= 64 && msub == 2)
+        gateup_body<(BM >= 64 ? 2 : 1), G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+    else
+        gateup_body<1, G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+}
+
+template <int MS, int G>
+__device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows, int K,
+                                          const moe_qmat &m, size_t ebase, const uint16_t *hsrc,
+                                          int orow0, bool routed, int nt, uint8_t *lds_a0,
+                                          uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint16_t *rowp[MS];
+    a_rows<MS>(rowp, hsrc, K, nullptr, 1, row0, rows);
+    const int ncol0 = nt * 256 + 64 * wave;  // this wave: columns [ncol0, ncol0 + 64)
+    const bool wave_active = ncol0 < a.d;
+    const int nbase = wave_active ? ncol0 : 0;
+    const int Kq = K >> 1, Kg = K / G;
+    BSrc src;
 #pragma unroll
-    for (int i = 0; i < ATile<BM>::kPer; ++i) {
-        const int m = (threadIdx.x >> 3) + i * (kGemmThreads / 8);
-        if (m < rows) {
-            const int tok = routed ? a.perm[row0 + m] / a.k : row0 + m;
-            rowp[i] = a.x + (size_t)tok * a.d;
-        } else {
-            rowp[i] = nullptr;
-        }
+    for (int q = 0; q < 4; ++q) {
+        const int r = 16 * q + (lane >> 2);
+        src.q[q] = m.q + (ebase + nbase + r) * Kq;
     }
-    const int ncol0 = nt * 128 + 32 * wave;  // first h column of this wave
-    const bool wave_active = ncol0 < N;
-    const int n = ncol0 + (lane & 31);
-    const size_t brow = ebase + (wave_active ? n : 0);
-    const int Kq = a.d >> 1, Kg = a.d / a.G;
-    BRow b0 = {mg->q + brow * Kq, mg->s + brow * Kg, mg->b + brow * Kg};
-    BRow b1 = {mu->q + brow * Kq, mu->s + brow * Kg, mu->b + brow * Kg};
-    f32x16 accg[MS], accu[MS];
-    mainloop<BM>(rowp, a.d, b0, b1, wave_active, a.G, rows, lds, accg, accu);
+    const size_t r0 = ebase + nbase + (lane & 31), r1 = r0 + 32;
+    src.s0 = m.s + r0 * Kg; src.b0 = m.b + r0 * Kg;
+    src.s1 = m.s + r1 * Kg; src.b1 = m.b + r1 * Kg;
+    src.kbytes = Kq;
+    src.ngroups = Kg;
+    f32x16 acc0[MS], acc1[MS];
+    mainloop<MS, G>(rowp, K, src, lds_a0, lds_a1, lds_b0, lds_b1, acc0, acc1);
     if (!wave_active) return;
     const int half = lane >> 5;
+    const int n = nbase + (lane & 31);
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int m = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (m < rows)
-                out[(size_t)(row0 + m) * N + n] = f32_to_bf16(silu(accg[i][r]) * accu[i][r]);
+            const int mm = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (mm >= rows) continue;
+            const float wr = routed ? a.topk_w[a.perm[row0 + mm]] : 1.0f;
+            uint16_t *o = a.obuf + (size_t)(orow0 + mm) * a.d;
+            o[n] = f32_to_bf16(wr * acc0[i][r]);
+            o[n + 32] = f32_to_bf16(wr * acc1[i][r]);
         }
 }
 
-template <int BM>
+template <int BM, int G>
 __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
 {
-    constexpr int MS = BM / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * BM * kLdsPitch];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[BM * kARow];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[BM * kARow];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kBBuf];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kBBuf];
     const int L = xcd_logical_block(blockIdx.x, a.nblk_pad);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     int row0, rows, K, nt;
     const moe_qmat *m;
     size_t ebase;
@@ -307,34 +520,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     } else {
         return;
     }
-    const uint16_t *rowp[ATile<BM>::kPer];
-#pragma unroll
-    for (int i = 0; i < ATile<BM>::kPer; ++i) {
-        const int mm = (threadIdx.x >> 3) + i * (kGemmThreads / 8);
-        rowp[i] = (mm < rows) ? hsrc + (size_t)(row0 + mm) * K : nullptr;
-    }
-    const int ncol0 = nt * 256 + 64 * wave;  // this wave: columns [ncol0, ncol0 + 64)
-    const bool wave_active = ncol0 < a.d;
-    const int n = ncol0 + (lane & 31);
-    const int Kq = K >> 1, Kg = K / a.G;
-    const size_t r0 = ebase + (wave_active ? n : 0), r1 = r0 + (wave_active ? 32 : 0);
-    BRow b0 = {m->q + r0 * Kq, m->s + r0 * Kg, m->b + r0 * Kg};
-    BRow b1 = {m->q + r1 * Kq, m->s + r1 * Kg, m->b + r1 * Kg};
-    f32x16 acc0[MS], acc1[MS];
-    mainloop<BM>(rowp, K, b0, b1, wave_active, a.G, rows, lds, acc0, acc1);
-    if (!wave_active) return;
-    const int half = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < MS; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int mm = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (mm >= rows) continue;
-            const float wr = routed ? a.topk_w[a.perm[row0 + mm]] : 1.0f;
-            uint16_t *o = a.obuf + (size_t)(orow0 + mm) * a.d;
-            o[n] = f32_to_bf16(wr * acc0[i][r]);
-            o[n + 32] = f32_to_bf16(wr * acc1[i][r]);
-        }
+    const int msub = (rows + 31) >> 5;
+    if (BM >= 128 && msub > 2)
+        down_body<(BM >= 128 ? 4 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+    else if (BM >= 64 && msub == 2)
+        down_body<(BM >= 64 ? 2 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+    else
+        down_body<1, G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
 }
 
 // one wave per token: 16-byte loads of the k routed rows and the shared row
@@ -370,7 +562,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__rest
     }
 }
 
-template <int BM>
+template <int BM, int G>
 static hipError_t launch_bm(const Plan &p, const uint16_t *x, const moe_weights &w,
                             const moe_routing &r, uint16_t *y, void *ws, hipStream_t s,
                             EventTrace *tr)
@@ -393,7 +585,7 @@ static hipError_t launch_bm(const Plan &p, const uint16_t *x, const moe_weights 
     g.nblk_s = shared_tiles * g.ntn_s;
     g.nblk_pad = (g.nblk_r + g.nblk_s + 7) & ~7;
     g.h_r = h_r; g.h_s = h_s;
-    launch(tr, moe_gateup_kernel<BM>, dim3(g.nblk_pad), dim3(kGemmThreads), 0, s, g);
+    launch(tr, moe_gateup_kernel<BM, G>, dim3(g.nblk_pad), dim3(kGemmThreads), 0, s, g);
 
     DownArgs dn;
     dn.h_r = h_r; dn.h_s = h_s; dn.perm = r.perm; dn.topk_w = r.topk_w;
@@ -405,11 +597,23 @@ static hipError_t launch_bm(const Plan &p, const uint16_t *x, const moe_weights 
     dn.nblk_r = (int)p.max_tiles * dn.ntn;
     dn.nblk_s = shared_tiles * dn.ntn;
     dn.nblk_pad = (dn.nblk_r + dn.nblk_s + 7) & ~7;
-    launch(tr, moe_down_kernel<BM>, dim3(dn.nblk_pad), dim3(kGemmThreads), 0, s, dn);
+    launch(tr, moe_down_kernel<BM, G>, dim3(dn.nblk_pad), dim3(kGemmThreads), 0, s, dn);
 
     launch(tr, moe_combine_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, (const uint16_t *)obuf,
            (const int32_t *)r.inv_perm, p.T, p.k, p.d, y);
     return hipGetLastError();
+}
+
+template <int BM>
+static hipError_t launch_g(const Plan &p, const uint16_t *x, const moe_weights &w,
+                           const moe_routing &r, uint16_t *y, void *ws, hipStream_t s,
+                           EventTrace *tr)
+{
+    switch (p.G) {
+    case 32: return launch_bm<BM, 32>(p, x, w, r, y, ws, s, tr);
+    case 64: return launch_bm<BM, 64>(p, x, w, r, y, ws, s, tr);
+    default: return launch_bm<BM, 128>(p, x, w, r, y, ws, s, tr);
+    }
 }
 
 hipError_t launch_ffn_gemm(const Plan &p, const uint16_t *x, const moe_weights &w,
@@ -417,9 +621,9 @@ hipError_t launch_ffn_gemm(const Plan &p, const uint16_t *x, const moe_weights &
                            EventTrace *tr)
 {
     switch (p.tile_m) {
-    case 32: return launch_bm<32>(p, x, w, r, y, ws, s, tr);
-    case 64: return launch_bm<64>(p, x, w, r, y, ws, s, tr);
-    default: return launch_bm<128>(p, x, w, r, y, ws, s, tr);
+    case 32: return launch_g<32>(p, x, w, r, y, ws, s, tr);
+    case 64: return launch_g<64>(p, x, w, r, y, ws, s, tr);
+    default: return launch_g<128>(p, x, w, r, y, ws, s, tr);
     }
 }
 

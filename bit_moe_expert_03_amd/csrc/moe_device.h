@@ -20,11 +20,22 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
     return __uint_as_float(bits16 << 16);
 }
 
-// byte i of v as fp32 (v_cvt_f32_ubyte{0..3})
+// byte I of v as fp32: one v_cvt_f32_ubyte{I}.  Written as inline asm so the
+// compiler cannot turn "byte I of a nibble-masked word" into a bit-field
+// extract followed by a byte-0 conversion (two instructions).
 template <int I>
 __device__ __forceinline__ float ubyte_f32(uint32_t v)
 {
-    return (float)((v >> (8 * I)) & 0xFFu);
+    float r;
+    if constexpr (I == 0)
+        __asm__("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
+    else if constexpr (I == 1)
+        __asm__("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
+    else if constexpr (I == 2)
+        __asm__("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
+    else
+        __asm__("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
+    return r;
 }
 
 // two fp32 -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32);

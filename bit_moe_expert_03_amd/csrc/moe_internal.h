@@ -21,6 +21,7 @@ struct Plan {
     int64_t A;          // assignments T*k
     int route_tb;       // tokens per route block
     int route_nb;       // route blocks
+    int route_nbp;      // route blocks rounded up to a multiple of 16 (histogram row pitch)
     int64_t max_tiles;  // length of the tile arrays
     // workspace carving (byte offsets)
     size_t off_hist, off_hr, off_hs, off_obuf, off_dech, ws_bytes;

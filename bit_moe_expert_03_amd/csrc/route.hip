@@ -25,15 +25,20 @@
 
 namespace moe {
 
-// hist layout: [E][NB] (expert-major); after the scan it holds, for expert e
-// and block b, the first sorted row of e's assignments that come from b.
+// hist layout: [E][NBP] (expert-major, NBP = route blocks rounded up to 16,
+// padding columns zero); after the scan it holds, for expert e and block b,
+// the first sorted row of e's assignments that come from block b.
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
-    const float *__restrict__ logits, int T, int E, int k, int tb, int nb,
+    const float *__restrict__ logits, int T, int E, int k, int tb, int nb, int nbp,
     int32_t *__restrict__ topk_ids, float *__restrict__ topk_w, int32_t *__restrict__ hist)
 {
     __shared__ int cnt[kMaxE];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if (tid < E) cnt[tid] = 0;
+    // block 0 zeroes the padding columns [nb, nbp) of every expert row
+    if (blockIdx.x == 0)
+        for (int i = tid; i < E * (nbp - nb); i += kRouteThreads)
+            hist[(size_t)(i / (nbp - nb)) * nbp + nb + i % (nbp - nb)] = 0;
     __syncthreads();
 
     const int t0 = blockIdx.x * tb;
@@ -61,11 +66,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         }
     }
     __syncthreads();
-    if (tid < E) hist[(size_t)tid * nb + blockIdx.x] = cnt[tid];
+    if (tid < E) hist[(size_t)tid * nbp + blockIdx.x] = cnt[tid];
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(
-    int32_t *__restrict__ hist, int nb, int E, int tile_m, int32_t *__restrict__ counts,
+    int32_t *__restrict__ hist, int nbp, int E, int tile_m, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ tile_expert, int32_t *__restrict__ tile_row0,
     int32_t *__restrict__ tile_rows, int32_t *__restrict__ num_tiles)
 {
@@ -74,13 +79,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(
     __shared__ int off[kMaxE + 4];
     __shared__ int tstart[kMaxE + 4];
     const int tid = threadIdx.x;
-    // 4 threads per expert, each a contiguous segment of the route blocks
+    // 4 threads per expert, each a contiguous quarter of the (16-padded) blocks,
+    // read 4 counts at a time
     const int e = tid >> 2, q = tid & 3;
-    const int seg = (nb + 3) >> 2;
-    const int b0 = min(nb, q * seg), b1 = min(nb, b0 + seg);
+    const int seg4 = nbp >> 4;  // int4 chunks per quarter
+    int4 *row = reinterpret_cast<int4 *>(hist + (size_t)e * nbp) + q * seg4;
     int s = 0;
-    if (e < E)
-        for (int b = b0; b < b1; ++b) s += hist[(size_t)e * nb + b];
+    if (e < E) {
+#pragma unroll 8
+        for (int i = 0; i < seg4; ++i) {
+            const int4 v = row[i];
+            s += v.x + v.y + v.z + v.w;
+        }
+    }
     part[tid] = s;
     __syncthreads();
     if (tid < kMaxE)
@@ -121,11 +132,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(
     if (e < E) {
         int base = off[e];
         for (int qq = 0; qq < q; ++qq) base += part[4 * e + qq];
-        for (int b = b0; b < b1; ++b) {
-            const size_t i = (size_t)e * nb + b;
-            const int c = hist[i];
-            hist[i] = base;
-            base += c;
+#pragma unroll 8
+        for (int i = 0; i < seg4; ++i) {
+            const int4 v = row[i];
+            int4 o;
+            o.x = base; base += v.x;
+            o.y = base; base += v.y;
+            o.z = base; base += v.z;
+            o.w = base; base += v.w;
+            row[i] = o;
         }
     }
     // block map: tile i belongs to the expert whose tile range holds it
@@ -143,14 +158,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
-    const int32_t *__restrict__ topk_ids, const int32_t *__restrict__ hist, int nb, int E,
+    const int32_t *__restrict__ topk_ids, const int32_t *__restrict__ hist, int nbp, int E,
     int64_t A, int chunk, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm)
 {
     constexpr int kWaves = kRouteThreads / kWave;
     __shared__ int base[kMaxE];
     __shared__ int wcnt[kWaves][kMaxE];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    if (tid < E) base[tid] = hist[(size_t)tid * nb + blockIdx.x];
+    if (tid < E) base[tid] = hist[(size_t)tid * nbp + blockIdx.x];
     const int64_t a0 = (int64_t)blockIdx.x * chunk;
     const int64_t a1 = min(A, a0 + chunk);
     const uint64_t lt_mask = (1ull << lane) - 1ull;
@@ -193,12 +208,12 @@ hipError_t launch_route(const Plan &p, const float *logits, const moe_routing &r
     int32_t *hist = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + p.off_hist);
     if (p.route_nb > 0)
         launch(tr, route_topk_kernel, dim3(p.route_nb), dim3(kRouteThreads), 0, s, logits, p.T, p.E,
-               p.k, p.route_tb, p.route_nb, r.topk_ids, r.topk_w, hist);
-    launch(tr, route_scan_kernel, dim3(1), dim3(kRouteThreads), 0, s, hist, p.route_nb, p.E,
+               p.k, p.route_tb, p.route_nb, p.route_nbp, r.topk_ids, r.topk_w, hist);
+    launch(tr, route_scan_kernel, dim3(1), dim3(kRouteThreads), 0, s, hist, p.route_nbp, p.E,
            p.tile_m, r.counts, r.offsets, r.tile_expert, r.tile_row0, r.tile_rows, r.num_tiles);
     if (p.route_nb > 0)
         launch(tr, route_scatter_kernel, dim3(p.route_nb), dim3(kRouteThreads), 0, s, r.topk_ids,
-               (const int32_t *)hist, p.route_nb, p.E, p.A, p.route_tb * p.k, r.perm, r.inv_perm);
+               (const int32_t *)hist, p.route_nbp, p.E, p.A, p.route_tb * p.k, r.perm, r.inv_perm);
     return hipGetLastError();
 }
 
