@@ -58,17 +58,15 @@ moe_status make_plan(const moe_dims *dm, Plan *p, const char **why)
     p->T = d.T; p->d = d.d; p->E = d.E; p->k = d.k; p->F = d.F; p->Fs = d.Fs; p->G = d.G;
     p->A = (int64_t)d.T * d.k;
     p->tile_m = d.tile_m ? d.tile_m : pick_tile_m(p->A, d.E);
-    // route chunks: at most kRouteMaxBlocks blocks, >= 16 tokens (one per wave)
-    int tb = (int)((d.T + kRouteMaxBlocks - 1) / kRouteMaxBlocks);
-    tb = ((tb + 15) / 16) * 16;
-    if (tb < 16) tb = 16;
+    // route chunks: 16 tokens per route block (one per wave of the top-k kernel)
+    const int tb = 16;
     p->route_tb = tb;
     p->route_nb = (d.T + tb - 1) / tb;
     p->route_nbp = (p->route_nb + 15) & ~15;
     p->max_tiles = (p->A + p->tile_m - 1) / p->tile_m + (p->A < d.E ? p->A : d.E);
     const int Fmax = d.F > d.Fs ? d.F : d.Fs;
     size_t off = 0;
-    p->off_hist = off; off = align_up(off + (size_t)d.E * p->route_nbp * 4);
+    p->off_hist = off; off = align_up(off + ((size_t)2 * d.E * p->route_nbp + d.E) * 4);  // counts, bases, totals
     p->off_hr = off;   off = align_up(off + (size_t)p->A * d.F * 2);
     p->off_hs = off;   off = align_up(off + (size_t)d.T * d.Fs * 2);
     p->off_obuf = off; off = align_up(off + (size_t)(p->A + d.T) * d.d * 2);
@@ -202,7 +200,7 @@ MOE_API moe_status moe_ffn(const moe_dims *dims, const uint16_t *x, const moe_we
 static int layer_kernels(const Plan &p)
 {
     if (p.T == 1) return 2;              // decode gate/up, decode down
-    if (p.T == 0) return 1;              // route scan only
+    if (p.T == 0) return 1;              // empty routing
     return 3 + 3;                        // route topk, scan, scatter; gate/up, down, combine
 }
 

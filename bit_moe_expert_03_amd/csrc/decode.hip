@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
     if (a.logits) {
         if (wave == 0) {
             TopK tk;
-            wave_topk(a.logits, a.E, a.k, tk);
+            wave_topk(load_logits(a.logits, a.E), a.E, a.k, tk);
             float ex[4], part = 0.f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {

@@ -12,10 +12,10 @@
 // decodes them there (fp32 fma, then a round-to-nearest-even pack to bf16)
 // and feeds v_mfma_f32_32x32x16_bf16 -- the bf16 weights never exist outside
 // the registers of one wave, and each weight is decoded once per block.
-// The activations (gathered token rows) are staged through a 3-deep LDS ring
-// (every wave of the block reads all of them); A loads are issued two steps
-// ahead through registers, B codes two steps ahead, so HBM latency hides
-// behind two steps of matrix-core work.
+// The activations (gathered token rows, read by every wave of the block) and
+// the 4-bit codes are copied global->LDS one step (A) and one pair of steps
+// (B) ahead, so the copies of the next step overlap the matrix-core work of
+// the current one.
 //
 // Kernels (stream-ordered, no host round trip):
 //   moe_gateup_kernel   routed tiles (rows gathered through perm) and shared
@@ -367,8 +367,7 @@ __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int r
     const uint16_t *rowp[MS];
     a_rows<MS>(rowp, a.x, a.d, routed ? a.perm : nullptr, a.k, row0, rows);
     const int ncol0 = nt * 128 + 32 * wave;  // first h column of this wave
-    const bool wave_active = ncol0 < N;
-    const int nbase = wave_active ? ncol0 : 0;
+    const int nbase = ncol0 < N ? ncol0 : 0;  // idle waves compute on valid rows
     const int Kq = a.d >> 1, Kg = a.d / G;
     BSrc src;
 #pragma unroll
@@ -384,17 +383,31 @@ __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int r
     src.ngroups = Kg;
     f32x16 accg[MS], accu[MS];
     mainloop<MS, G>(rowp, a.d, src, lds_a0, lds_a1, lds_b0, lds_b1, accg, accu);
-    if (!wave_active) return;
+    // epilogue: h = bf16(silu(g) * u) into an LDS tile [MS*32 rows][128 cols]
+    // (rows 0..63 in lds_b0, 64..127 in lds_b1, 256-byte rows), then 16-byte
+    // coalesced stores of whole 256-byte row segments
+    block_sync();  // every wave is done reading the last A stage and B buffer
     const int half = lane >> 5;
-    const int n = nbase + (lane & 31);
+    const int n = lane & 31;
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int m = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (m < rows)
-                out[(size_t)(row0 + m) * N + n] = f32_to_bf16(silu(accg[i][r]) * accu[i][r]);
+            uint8_t *rowb = (m < 64 ? lds_b0 : lds_b1) + (m & 63) * 256;
+            *reinterpret_cast<uint16_t *>(rowb + (32 * wave + n) * 2) = f32_to_bf16(silu(accg[i][r]) * accu[i][r]);
         }
+    block_sync();
+    const int chunk = threadIdx.x & 15, col = nt * 128 + chunk * 8;
+#pragma unroll
+    for (int it = 0; it < MS * 2; ++it) {
+        const int m = (threadIdx.x >> 4) + 16 * it;
+        if (m < rows && col < N) {
+            const uint8_t *rowb = (m < 64 ? lds_b0 : lds_b1) + (m & 63) * 256;
+            *reinterpret_cast<uint4 *>(out + (size_t)(row0 + m) * N + col) =
+                *reinterpret_cast<const uint4 *>(rowb + chunk * 16);
+        }
+    }
 }
 
 template <int BM, int G>
@@ -446,14 +459,17 @@ template <int MS, int G>
 __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows, int K,
                                           const moe_qmat &m, size_t ebase, const uint16_t *hsrc,
                                           int orow0, bool routed, int nt, uint8_t *lds_a0,
-                                          uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1)
+                                          uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1,
+                                          float *row_w)
 {
+    // routing weight of every routed row of the tile (read in the epilogue)
+    if (routed && threadIdx.x < MS * 32)
+        row_w[threadIdx.x] = a.topk_w[a.perm[row0 + min((int)threadIdx.x, rows - 1)]];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint16_t *rowp[MS];
     a_rows<MS>(rowp, hsrc, K, nullptr, 1, row0, rows);
     const int ncol0 = nt * 256 + 64 * wave;  // this wave: columns [ncol0, ncol0 + 64)
-    const bool wave_active = ncol0 < a.d;
-    const int nbase = wave_active ? ncol0 : 0;
+    const int nbase = ncol0 < a.d ? ncol0 : 0;  // idle waves compute on valid rows
     const int Kq = K >> 1, Kg = K / G;
     BSrc src;
 #pragma unroll
@@ -468,20 +484,34 @@ __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows,
     src.ngroups = Kg;
     f32x16 acc0[MS], acc1[MS];
     mainloop<MS, G>(rowp, K, src, lds_a0, lds_a1, lds_b0, lds_b1, acc0, acc1);
-    if (!wave_active) return;
+    // epilogue: o = w_route * acc as bf16 into an LDS tile [MS*32 rows][256
+    // cols] (512-byte rows; rows 32 q .. 32 q + 31 in the q-th of the four
+    // LDS objects), then 16-byte coalesced stores of 512-byte row segments
+    block_sync();
     const int half = lane >> 5;
-    const int n = nbase + (lane & 31);
+    const int n = lane & 31;
+    uint8_t *const part[4] = {lds_b0, lds_b1, lds_a0, lds_a1};
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int mm = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (mm >= rows) continue;
-            const float wr = routed ? a.topk_w[a.perm[row0 + mm]] : 1.0f;
-            uint16_t *o = a.obuf + (size_t)(orow0 + mm) * a.d;
-            o[n] = f32_to_bf16(wr * acc0[i][r]);
-            o[n + 32] = f32_to_bf16(wr * acc1[i][r]);
+            const int m = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+            const float wr = routed ? row_w[m] : 1.0f;
+            uint8_t *rowb = part[i] + (m & 31) * 512;
+            *reinterpret_cast<uint16_t *>(rowb + (64 * wave + n) * 2) = f32_to_bf16(wr * acc0[i][r]);
+            *reinterpret_cast<uint16_t *>(rowb + (64 * wave + n + 32) * 2) = f32_to_bf16(wr * acc1[i][r]);
         }
+    block_sync();
+    const int chunk = threadIdx.x & 31, col = nt * 256 + chunk * 8;
+#pragma unroll
+    for (int it = 0; it < MS * 4; ++it) {
+        const int m = (threadIdx.x >> 5) + 8 * it;
+        if (m < rows && col < a.d) {
+            const uint8_t *rowb = part[m >> 5] + (m & 31) * 512;
+            *reinterpret_cast<uint4 *>(a.obuf + (size_t)(orow0 + m) * a.d + col) =
+                *reinterpret_cast<const uint4 *>(rowb + chunk * 16);
+        }
+    }
 }
 
 template <int BM, int G>
@@ -491,6 +521,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[BM * kARow];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kBBuf];
+    __shared__ float row_w[kMaxMS * 32];
     const int L = xcd_logical_block(blockIdx.x, a.nblk_pad);
     int row0, rows, K, nt;
     const moe_qmat *m;
@@ -522,11 +553,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     }
     const int msub = (rows + 31) >> 5;
     if (BM >= 128 && msub > 2)
-        down_body<(BM >= 128 ? 4 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+        down_body<(BM >= 128 ? 4 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, row_w);
     else if (BM >= 64 && msub == 2)
-        down_body<(BM >= 64 ? 2 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+        down_body<(BM >= 64 ? 2 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, row_w);
     else
-        down_body<1, G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+        down_body<1, G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, row_w);
 }
 
 // one wave per token: 16-byte loads of the k routed rows and the shared row

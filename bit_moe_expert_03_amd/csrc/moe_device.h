@@ -150,14 +150,31 @@ struct TopK {
     float lmax;
 };
 
-__device__ __forceinline__ void wave_topk(const float *__restrict__ L, int E, int k, TopK &out)
+// logits of experts 4 lane .. 4 lane + 3 of one row (rows past E read as 0)
+struct LogitQuad {
+    float v[4];
+};
+
+__device__ __forceinline__ LogitQuad load_logits(const float *__restrict__ L, int E)
+{
+    const int lane = threadIdx.x & 63;
+    LogitQuad q;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int e = 4 * lane + c;
+        q.v[c] = e < E ? L[e] : 0.f;
+    }
+    return q;
+}
+
+__device__ __forceinline__ void wave_topk(const LogitQuad &lq, int E, int k, TopK &out)
 {
     const int lane = threadIdx.x & 63;
     uint32_t key[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int e = 4 * lane + c;
-        key[c] = (e < E) ? logit_key(L[e]) : 0u;  // 0: no expert (finite keys are > 0)
+        key[c] = (e < E) ? logit_key(lq.v[c]) : 0u;  // 0: no expert (finite keys are > 0)
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) { out.id[c] = 0; out.logit[c] = 0.f; }

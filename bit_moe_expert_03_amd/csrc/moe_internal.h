@@ -12,7 +12,6 @@
 namespace moe {
 
 constexpr int kRouteThreads = 1024;  // routing kernels: 16 waves per block
-constexpr int kRouteMaxBlocks = 512; // cap on route blocks (bounds the scan's input)
 constexpr int kMaxE = 256;
 
 // Everything derived from moe_dims that the launchers need.

@@ -159,7 +159,7 @@ MOE_API moe_status moe_layer(const moe_dims *dims, const float *logits, const ui
 /* Host-only, pure.  Number of kernels one moe_layer call launches for these
  * dims, in launch order: T == 1: decode gate/up (with routing), decode down;
  * T >= 2: route top-k, route scan, route scatter, gate/up GEMM, down GEMM
- * (routed and shared rows), combine; T == 0: route scan.  0 for invalid
+ * (routed and shared rows), combine; T == 0: empty routing.  0 for invalid
  * dims. */
 MOE_API int32_t moe_layer_kernels(const moe_dims *dims);
 
