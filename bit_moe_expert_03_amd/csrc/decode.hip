@@ -7,29 +7,38 @@
 // prefill and decode get different treatment").
 //
 // Two kernels per layer:
-//   decode_gateup_kernel  top-k of the token's logits (wave 0 of every block,
-//                         DPP maxima; block 0 also writes the routing
-//                         outputs), then h_j[n] = silu(W_gate,j[n] . x) *
-//                         (W_up,j[n] . x) for the shared expert and the k
-//                         routed ones, fp32.  The shared expert's rows come
-//                         first in the work order and their loads are issued
-//                         before the routing result is waited for;
+//   decode_gateup_kernel  block 0: top-k + softmax of the token's logits and
+//                         the routing outputs.  Every other wave owns
+//                         P (gate, up) row pairs of one expert slot
+//                         and writes h_j[n] = bf16(silu(W_gate,j[n] . x) *
+//                         (W_up,j[n] . x)).  A wave of routed slot j needs
+//                         only the expert of rank j, so it runs the top-k
+//                         rounds 0..j itself (no block barrier) and issues
+//                         its loads as soon as that expert is known; the
+//                         shared expert's waves load at once.  Slots are
+//                         ordered k-1 .. 0, shared last, so the waves with
+//                         the longest top-k are dispatched first.
 //   decode_down_kernel    y[i] = sum_j w_j (W_down,j[i] . h_j) + W_sdown[i] . h_s,
-//                         one block per 4 output rows, one wave per 64
-//                         chunks of the concatenated hidden vector.
+//                         kDownRows output rows per block; lane = one
+//                         32-element chunk of the concatenated hidden vector
+//                         (shared expert first, its loads need no routing).
 //
-// The 4-bit decode uses the factored form of one affine group,
+// The 4-bit dot products use the factored form of one affine group,
 //   sum_i (s q_i + b) x_i = s * sum_i q_i x_i + b * sum_i x_i,
-// so the codes are converted to fp32 and multiplied by x, and the scale and
-// bias are applied once per 32-element chunk.  No bf16 rounding of weights.
+// with the codes turned into exact bf16 values 128 + q (one byte permute
+// against the constant byte 0x43 yields two of them) and multiplied with
+// v_dot2_f32_bf16 (fp32 accumulation); the offset is folded into the bias
+// term: s * sum (128 + q_i) x_i + (b - 128 s) * sum x_i.  The codes of one
+// 32-bit word pair up as (e0, e2), (e4, e6), (e1, e3), (e5, e7); the vector
+// operand is permuted once per lane into the same order.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
 constexpr int kDecThreads = 256;  // 4 waves per block
-constexpr int kDecPairs = 2;      // (gate, up) row pairs per wave
-constexpr int kDownRows = 4;      // output rows per down block
+constexpr int kDownRows = 8;      // output rows per down block
+constexpr int kDownMaxThreads = 512;
 
 struct DecodeArgs {
     const float *logits;  // [1][E] or null (routing given in r)
@@ -37,12 +46,70 @@ struct DecodeArgs {
     moe_weights w;
     moe_routing r;
     int d, E, k, F, Fs, G, Fmax;
-    float *h;             // [k+1][Fmax] fp32 workspace: slots 0..k-1 routed, k shared
+    int wps_r, wps_s;     // work waves per routed slot, for the shared expert
+    uint16_t *h;          // [k+1][Fmax] bf16 workspace: slots 0..k-1 routed, k shared
     uint16_t *y;          // [1][d]
 };
 
-// routing outputs of the single token (block 0 only): ids, weights, the
-// one-row-per-expert histogram, its scan, the sorted order and the tiles
+// ---- packed 4-bit dot products ---------------------------------------------
+
+// 32 elements of a bf16 vector as the bf16 pairs in the order dot_codes32()
+// pairs the codes, and their fp32 sum
+struct VecChunk {
+    uint32_t p[16];
+    float sum;
+};
+
+__device__ __forceinline__ void vec_chunk(const uint4 (&w)[4], VecChunk &v)
+{
+    v.sum = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t w0 = w[g].x, w1 = w[g].y, w2 = w[g].z, w3 = w[g].w;  // (x0,x1) .. (x6,x7)
+        v.p[4 * g + 0] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);  // (x0, x2)
+        v.p[4 * g + 1] = __builtin_amdgcn_perm(w3, w2, 0x05040100u);  // (x4, x6)
+        v.p[4 * g + 2] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);  // (x1, x3)
+        v.p[4 * g + 3] = __builtin_amdgcn_perm(w3, w2, 0x07060302u);  // (x5, x7)
+        const uint32_t ws[4] = {w0, w1, w2, w3};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v.sum += bf16_to_f32(ws[i] & 0xFFFFu) + bf16_to_f32(ws[i] >> 16);
+    }
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// sum over the chunk of (128 + q_i) * v_i for the 32 codes in q
+__device__ __forceinline__ float dot_codes32(const uint4 &q, const VecChunk &v)
+{
+    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = wd[g] & 0x0F0F0F0Fu;         // e0, e2, e4, e6 (one per byte)
+        const uint32_t hi = (wd[g] >> 4) & 0x0F0F0F0Fu;  // e1, e3, e5, e7
+        // bytes (e, 0x43, e', 0x43): the bf16 pair (128 + e, 128 + e')
+        acc = dot2_bf16(__builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u), v.p[4 * g + 0], acc);
+        acc = dot2_bf16(__builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u), v.p[4 * g + 1], acc);
+        acc = dot2_bf16(__builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u), v.p[4 * g + 2], acc);
+        acc = dot2_bf16(__builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u), v.p[4 * g + 3], acc);
+    }
+    return acc;
+}
+
+// one chunk's share of an affine-group dot product: s * sum q v + b * sum v
+__device__ __forceinline__ float chunk_term(float dq128, const VecChunk &v, uint16_t s, uint16_t b)
+{
+    const float sf = bf16_to_f32(s), bf = bf16_to_f32(b);
+    return sf * dq128 + (bf - 128.0f * sf) * v.sum;
+}
+
+// ---- routing -----------------------------------------------------------------
+
+// routing outputs of the single token: ids, weights, the one-row-per-expert
+// histogram, its scan, the sorted order and the tiles
 __device__ void decode_write_routing(const DecodeArgs &a, const int *s_ids, const float *s_w)
 {
     const int tid = threadIdx.x;
@@ -67,35 +134,73 @@ __device__ void decode_write_routing(const DecodeArgs &a, const int *s_ids, cons
     if (tid == 0) *r.num_tiles = a.k;
 }
 
-// raw operands of one (gate, up) row pair for one 32-element chunk
-struct PairRaw {
-    uint4 qg, qu;
-    uint16_t sg, bg, su, bu;
-};
-
-__device__ __forceinline__ void load_pair(PairRaw &r, const moe_qmat &mg, const moe_qmat &mu, size_t row,
-                                          int c, int d, int G)
-{
-    const size_t qo = row * (size_t)(d >> 1) + (size_t)c * 16;
-    r.qg = *reinterpret_cast<const uint4 *>(mg.q + qo);
-    r.qu = *reinterpret_cast<const uint4 *>(mu.q + qo);
-    const size_t gi = row * (size_t)(d / G) + (size_t)(c * 32) / G;
-    r.sg = mg.s[gi]; r.bg = mg.b[gi];
-    r.su = mu.s[gi]; r.bu = mu.b[gi];
-}
-
-// NCH = 32-element chunks of x per lane (d <= 2048 * NCH)
-template <int NCH>
-__global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a)
+// block 0 of the gate/up grid: top-k, softmax over the k chosen logits
+__device__ void decode_routing_block(const DecodeArgs &a)
 {
     __shared__ int s_ids[kMaxE];
     __shared__ float s_w[kMaxE];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int nchunk = a.d >> 5;
-    const int npairs = a.Fs + a.k * a.F;
-    const int p0 = (blockIdx.x * (kDecThreads / kWave) + wave) * kDecPairs;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (wave == 0) {
+        TopK tk;
+        wave_topk(load_logits(a.logits, a.E), a.E, a.k, tk);
+        float ex[4], part = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int j = lane + 64 * c;
+            ex[c] = (j < a.k) ? expf(tk.logit[c] - tk.lmax) : 0.f;
+            part += ex[c];
+        }
+        const float inv = 1.0f / wave_sum(part);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int j = lane + 64 * c;
+            if (j < a.k) { s_ids[j] = tk.id[c]; s_w[j] = ex[c] * inv; }
+        }
+    }
+    __syncthreads();
+    decode_write_routing(a, s_ids, s_w);
+}
 
-    // x chunks of this lane: chunk c = lane + 64 i covers x[32c, 32c+32)
+// ---- gate/up -------------------------------------------------------------------
+
+// raw operands of one row for one 32-element chunk
+struct RowRaw {
+    uint4 q;
+    uint16_t s, b;
+};
+
+__device__ __forceinline__ void load_row(RowRaw &r, const moe_qmat &m, size_t row, int c, int d, int G)
+{
+    r.q = *reinterpret_cast<const uint4 *>(m.q + row * (size_t)(d >> 1) + (size_t)c * 16);
+    const size_t gi = row * (size_t)(d / G) + (size_t)(c * 32) / G;
+    r.s = m.s[gi];
+    r.b = m.b[gi];
+}
+
+// NCH = 32-element chunks of x per lane (d <= 2048 * NCH); P row pairs per wave
+template <int NCH, int P>
+__global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a)
+{
+    if (blockIdx.x == 0) {
+        if (a.logits) decode_routing_block(a);
+        return;
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int gw = (blockIdx.x - 1) * (kDecThreads / kWave) + wave;  // work wave
+    const int nchunk = a.d >> 5;
+    int slot, n0;
+    if (gw < a.k * a.wps_r) {
+        slot = a.k - 1 - gw / a.wps_r;
+        n0 = (gw % a.wps_r) * P;
+    } else if (gw < a.k * a.wps_r + a.wps_s) {
+        slot = a.k;
+        n0 = (gw - a.k * a.wps_r) * P;
+    } else {
+        return;
+    }
+    const bool shared = slot == a.k;
+
+    // this lane's chunks of x: chunk c = lane + 64 i covers x[32c, 32c+32)
     uint4 xr[NCH][4];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -106,165 +211,107 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
             for (int v = 0; v < 4; ++v) xr[i][v] = xp[v];
         }
     }
-    // shared-expert rows do not depend on the routing: load them first
-    PairRaw raw[kDecPairs][NCH];
-#pragma unroll
-    for (int pi = 0; pi < kDecPairs; ++pi) {
-        const int p = p0 + pi;
-        if (p < a.Fs) {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int c = lane + 64 * i;
-                if (c < nchunk) load_pair(raw[pi][i], a.w.sgate, a.w.sup, (size_t)p, c, a.d, a.G);
-            }
-        }
-    }
-    if (a.logits) {
-        if (wave == 0) {
-            TopK tk;
-            wave_topk(load_logits(a.logits, a.E), a.E, a.k, tk);
-            float ex[4], part = 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int j = lane + 64 * c;
-                ex[c] = (j < a.k) ? expf(tk.logit[c] - tk.lmax) : 0.f;
-                part += ex[c];
-            }
-            const float inv = 1.0f / wave_sum(part);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int j = lane + 64 * c;
-                if (j < a.k) { s_ids[j] = tk.id[c]; s_w[j] = ex[c] * inv; }
-            }
-        }
-        __syncthreads();
-        if (blockIdx.x == 0) decode_write_routing(a, s_ids, s_w);
+    RowRaw rg[P][NCH], ru[P][NCH];
+    const moe_qmat &mg = shared ? a.w.sgate : a.w.gate;
+    const moe_qmat &mu = shared ? a.w.sup : a.w.up;
+    size_t row0;
+    if (shared) {
+        row0 = (size_t)n0;
     } else {
-        for (int j = tid; j < a.k; j += kDecThreads) s_ids[j] = a.r.topk_ids[j];
-        __syncthreads();
+        int e;
+        if (a.logits) {
+            uint32_t key[4];
+            const LogitQuad lq = load_logits(a.logits, a.E);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) key[c] = (4 * lane + c < a.E) ? logit_key(lq.v[c]) : 0u;
+            e = wave_rank_expert(key, slot);
+        } else {
+            e = a.r.topk_ids[slot];
+        }
+        row0 = (size_t)e * a.F + n0;
     }
 #pragma unroll
-    for (int pi = 0; pi < kDecPairs; ++pi) {
-        const int p = p0 + pi;
-        if (p >= a.Fs && p < npairs) {
-            const int j = (p - a.Fs) / a.F, n = (p - a.Fs) - j * a.F;
-            const size_t row = (size_t)s_ids[j] * a.F + n;
+    for (int pi = 0; pi < P; ++pi)
 #pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int c = lane + 64 * i;
-                if (c < nchunk) load_pair(raw[pi][i], a.w.gate, a.w.up, row, c, a.d, a.G);
+        for (int i = 0; i < NCH; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nchunk) {
+                load_row(rg[pi][i], mg, row0 + pi, c, a.d, a.G);
+                load_row(ru[pi][i], mu, row0 + pi, c, a.d, a.G);
             }
         }
-    }
-    float accg[kDecPairs], accu[kDecPairs];
+    float accg[P], accu[P];
 #pragma unroll
-    for (int pi = 0; pi < kDecPairs; ++pi) { accg[pi] = 0.f; accu[pi] = 0.f; }
+    for (int pi = 0; pi < P; ++pi) { accg[pi] = 0.f; accu[pi] = 0.f; }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int c = lane + 64 * i;
         if (c >= nchunk) continue;
-        float xv[32], xs = 0.f;
+        VecChunk xv;
+        vec_chunk(xr[i], xv);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const uint32_t wd[4] = {xr[i][v].x, xr[i][v].y, xr[i][v].z, xr[i][v].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                xv[8 * v + 2 * q] = bf16_to_f32(wd[q] & 0xFFFFu);
-                xv[8 * v + 2 * q + 1] = bf16_to_f32(wd[q] >> 16);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < 32; ++q) xs += xv[q];
-#pragma unroll
-        for (int pi = 0; pi < kDecPairs; ++pi) {
-            const PairRaw &r = raw[pi][i];
-            float dg = 0.f, du = 0.f;
-            dg = dot8_codes(r.qg.x, xv + 0, dg);
-            dg = dot8_codes(r.qg.y, xv + 8, dg);
-            dg = dot8_codes(r.qg.z, xv + 16, dg);
-            dg = dot8_codes(r.qg.w, xv + 24, dg);
-            du = dot8_codes(r.qu.x, xv + 0, du);
-            du = dot8_codes(r.qu.y, xv + 8, du);
-            du = dot8_codes(r.qu.z, xv + 16, du);
-            du = dot8_codes(r.qu.w, xv + 24, du);
-            accg[pi] += bf16_to_f32(r.sg) * dg + bf16_to_f32(r.bg) * xs;
-            accu[pi] += bf16_to_f32(r.su) * du + bf16_to_f32(r.bu) * xs;
+        for (int pi = 0; pi < P; ++pi) {
+            accg[pi] += chunk_term(dot_codes32(rg[pi][i].q, xv), xv, rg[pi][i].s, rg[pi][i].b);
+            accu[pi] += chunk_term(dot_codes32(ru[pi][i].q, xv), xv, ru[pi][i].s, ru[pi][i].b);
         }
     }
+    uint16_t *hrow = a.h + (size_t)slot * a.Fmax + n0;
 #pragma unroll
-    for (int pi = 0; pi < kDecPairs; ++pi) {
-        const int p = p0 + pi;
+    for (int pi = 0; pi < P; ++pi) {
         const float g = wave_sum(accg[pi]);
         const float u = wave_sum(accu[pi]);
-        if (lane == 0 && p < npairs) {
-            int j, n;
-            if (p < a.Fs) { j = a.k; n = p; }
-            else { j = (p - a.Fs) / a.F; n = (p - a.Fs) - j * a.F; }
-            a.h[(size_t)j * a.Fmax + n] = silu(g) * u;
-        }
+        if (lane == 0) hrow[pi] = f32_to_bf16(silu(g) * u);
     }
 }
 
-// One block = kDownRows output rows; wave w takes the 32-wide chunks
-// w*64 + lane, w*64 + lane + 64*nw, ... of [h_0 .. h_{k-1}, h_s].
-__global__ void decode_down_kernel(DecodeArgs a)
+// ---- down ---------------------------------------------------------------------
+
+// One block = kDownRows output rows; lane chunks c = tid, tid + blockDim, ...
+// of [h_s, h_0 .. h_{k-1}] in 32-element chunks.
+__global__ __launch_bounds__(kDownMaxThreads) void decode_down_kernel(DecodeArgs a)
 {
-    __shared__ float red[16][kDownRows];
-    __shared__ int s_ids[kMaxE];
-    __shared__ float s_w[kMaxE];
+    __shared__ float red[kDownMaxThreads / kWave][kDownRows];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nw = blockDim.x >> 6;
-    for (int j = tid; j < a.k; j += blockDim.x) { s_ids[j] = a.r.topk_ids[j]; s_w[j] = a.r.topk_w[j]; }
-    __syncthreads();
     const int row0 = blockIdx.x * kDownRows;
     const int cF = a.F >> 5, cFs = a.Fs >> 5;
     const int nchunks = a.k * cF + cFs;
     float acc[kDownRows];
 #pragma unroll
     for (int r = 0; r < kDownRows; ++r) acc[r] = 0.f;
-    for (int c = wave * kWave + lane; c < nchunks; c += nw * kWave) {
+    for (int c = tid; c < nchunks; c += blockDim.x) {
         int j, f0, Fw;
         const moe_qmat *m;
         size_t ebase;
         float wj;
-        if (c < a.k * cF) {
-            j = c / cF; f0 = (c - j * cF) * 32; Fw = a.F; m = &a.w.down;
-            ebase = (size_t)s_ids[j] * a.d;
-            wj = s_w[j];
-        } else {
-            j = a.k; f0 = (c - a.k * cF) * 32; Fw = a.Fs; m = &a.w.sdown;
+        if (c < cFs) {  // shared expert: no routing needed
+            j = a.k; f0 = c * 32; Fw = a.Fs; m = &a.w.sdown;
             ebase = 0;
             wj = 1.0f;
+        } else {
+            j = (c - cFs) / cF; f0 = (c - cFs - j * cF) * 32; Fw = a.F; m = &a.w.down;
+            ebase = (size_t)a.r.topk_ids[j] * a.d;
+            wj = a.r.topk_w[j];
         }
         uint4 q[kDownRows];
-        uint16_t sb[kDownRows][2];
+        uint16_t s[kDownRows], b[kDownRows];
         const int grp = f0 / a.G;
 #pragma unroll
         for (int r = 0; r < kDownRows; ++r) {
             const size_t row = ebase + min(row0 + r, a.d - 1);
             q[r] = *reinterpret_cast<const uint4 *>(m->q + row * (size_t)(Fw >> 1) + (f0 >> 1));
             const size_t gi = row * (size_t)(Fw / a.G) + grp;
-            sb[r][0] = m->s[gi];
-            sb[r][1] = m->b[gi];
+            s[r] = m->s[gi];
+            b[r] = m->b[gi];
         }
-        float hv[32], hs = 0.f;
-        const float4 *hp = reinterpret_cast<const float4 *>(a.h + (size_t)j * a.Fmax + f0);
+        uint4 hr[4];
+        const uint4 *hp = reinterpret_cast<const uint4 *>(a.h + (size_t)j * a.Fmax + f0);
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const float4 t = hp[v];
-            hv[4 * v] = t.x; hv[4 * v + 1] = t.y; hv[4 * v + 2] = t.z; hv[4 * v + 3] = t.w;
-        }
+        for (int v = 0; v < 4; ++v) hr[v] = hp[v];
+        VecChunk hv;
+        vec_chunk(hr, hv);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) hs += hv[i];
-#pragma unroll
-        for (int r = 0; r < kDownRows; ++r) {
-            float dq = 0.f;
-            dq = dot8_codes(q[r].x, hv + 0, dq);
-            dq = dot8_codes(q[r].y, hv + 8, dq);
-            dq = dot8_codes(q[r].z, hv + 16, dq);
-            dq = dot8_codes(q[r].w, hv + 24, dq);
-            acc[r] += wj * (bf16_to_f32(sb[r][0]) * dq + bf16_to_f32(sb[r][1]) * hs);
-        }
+        for (int r = 0; r < kDownRows; ++r) acc[r] += wj * chunk_term(dot_codes32(q[r], hv), hv, s[r], b[r]);
     }
 #pragma unroll
     for (int r = 0; r < kDownRows; ++r) {
@@ -279,6 +326,16 @@ __global__ void decode_down_kernel(DecodeArgs a)
     }
 }
 
+template <int NCH, int P>
+static void launch_gateup(EventTrace *tr, DecodeArgs &a, hipStream_t s)
+{
+    a.wps_r = a.F / P;
+    a.wps_s = a.Fs / P;
+    const int waves = a.k * a.wps_r + a.wps_s;
+    const int nb = 1 + (waves + kDecThreads / kWave - 1) / (kDecThreads / kWave);
+    launch(tr, decode_gateup_kernel<NCH, P>, dim3(nb), dim3(kDecThreads), 0, s, a);
+}
+
 hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
                          const moe_weights &w, const moe_routing &r, uint16_t *y, void *ws,
                          hipStream_t s, EventTrace *tr)
@@ -290,23 +347,21 @@ hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
     a.r = r;
     a.d = p.d; a.E = p.E; a.k = p.k; a.F = p.F; a.Fs = p.Fs; a.G = p.G;
     a.Fmax = p.F > p.Fs ? p.F : p.Fs;
-    a.h = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_dech);
+    a.h = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + p.off_dech);
     a.y = y;
-    const int npairs = p.k * p.F + p.Fs;
-    const int per_block = (kDecThreads / kWave) * kDecPairs;
-    const int nb1 = (npairs + per_block - 1) / per_block;
+    // F and Fs are multiples of 64, so every P below divides both
     const int nch = (p.d / 32 + kWave - 1) / kWave;
     if (nch <= 1)
-        launch(tr, decode_gateup_kernel<1>, dim3(nb1), dim3(kDecThreads), 0, s, a);
+        launch_gateup<1, 4>(tr, a, s);
     else if (nch <= 2)
-        launch(tr, decode_gateup_kernel<2>, dim3(nb1), dim3(kDecThreads), 0, s, a);
+        launch_gateup<2, 4>(tr, a, s);
     else if (nch <= 4)
-        launch(tr, decode_gateup_kernel<4>, dim3(nb1), dim3(kDecThreads), 0, s, a);
+        launch_gateup<4, 2>(tr, a, s);
     else
-        launch(tr, decode_gateup_kernel<8>, dim3(nb1), dim3(kDecThreads), 0, s, a);
+        launch_gateup<8, 1>(tr, a, s);
     const int nchunks = p.k * (p.F >> 5) + (p.Fs >> 5);
     int nw = (nchunks + kWave - 1) / kWave;
-    nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
+    nw = nw < 1 ? 1 : (nw > kDownMaxThreads / kWave ? kDownMaxThreads / kWave : nw);
     const int nb2 = (p.d + kDownRows - 1) / kDownRows;
     launch(tr, decode_down_kernel, dim3(nb2), dim3(nw * kWave), 0, s, a);
     return hipGetLastError();

@@ -167,6 +167,29 @@ __device__ __forceinline__ LogitQuad load_logits(const float *__restrict__ L, in
     return q;
 }
 
+// One selection round over the wave's keys (lane l holds experts 4l .. 4l+3;
+// key 0 = no expert): the largest key m and its expert id (ties to the lower
+// id); the chosen key is cleared.
+__device__ __forceinline__ int topk_round(uint32_t (&key)[4], uint32_t &m)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t local = max(max(key[0], key[1]), max(key[2], key[3]));
+    m = wave_max_u32(local);
+    const uint64_t holders = __ballot(local == m);
+    const int wl = __ffsll((unsigned long long)holders) - 1;  // lowest lane with the max
+    int slot = 3;
+#pragma unroll
+    for (int c = 2; c >= 0; --c)
+        if (key[c] == m) slot = c;
+    slot = __builtin_amdgcn_readlane(slot, wl);
+    if (lane == wl) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (c == slot) key[c] = 0u;
+    }
+    return 4 * wl + slot;
+}
+
 __device__ __forceinline__ void wave_topk(const LogitQuad &lq, int E, int k, TopK &out)
 {
     const int lane = threadIdx.x & 63;
@@ -180,26 +203,26 @@ __device__ __forceinline__ void wave_topk(const LogitQuad &lq, int E, int k, Top
     for (int c = 0; c < 4; ++c) { out.id[c] = 0; out.logit[c] = 0.f; }
     out.lmax = 0.f;
     for (int j = 0; j < k; ++j) {
-        const uint32_t local = max(max(key[0], key[1]), max(key[2], key[3]));
-        const uint32_t m = wave_max_u32(local);
-        const uint64_t holders = __ballot(local == m);
-        const int wl = __ffsll((unsigned long long)holders) - 1;  // lowest lane with the max
-        int slot = 3;
-#pragma unroll
-        for (int c = 2; c >= 0; --c)
-            if (key[c] == m) slot = c;
-        slot = __builtin_amdgcn_readlane(slot, wl);
-        if (lane == wl) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (c == slot) key[c] = 0u;
-        }
+        uint32_t m;
+        const int id = topk_round(key, m);
         const float l = key_logit(m);
         if (j == 0) out.lmax = l;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            if (j == lane + 64 * c) { out.id[c] = 4 * wl + slot; out.logit[c] = l; }
+            if (j == lane + 64 * c) { out.id[c] = id; out.logit[c] = l; }
     }
+}
+
+// Expert of rank j (0-based, ties to the lower id) among the wave's keys:
+// rounds 0 .. j of the selection above, nothing more (keys are consumed).
+__device__ __forceinline__ int wave_rank_expert(uint32_t (&key)[4], int j)
+{
+    int id = 0;
+    for (int r = 0; r <= j; ++r) {
+        uint32_t m;
+        id = topk_round(key, m);
+    }
+    return id;
 }
 
 __device__ __forceinline__ float silu(float z)
