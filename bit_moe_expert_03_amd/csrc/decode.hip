@@ -37,7 +37,7 @@
 namespace moe {
 
 constexpr int kDecThreads = 256;  // 4 waves per block
-constexpr int kDownRows = 8;      // output rows per down block
+constexpr int kDownRows = 2;      // output rows per down block
 constexpr int kDownMaxThreads = 512;
 
 struct DecodeArgs {
@@ -352,9 +352,9 @@ hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
     // F and Fs are multiples of 64, so every P below divides both
     const int nch = (p.d / 32 + kWave - 1) / kWave;
     if (nch <= 1)
-        launch_gateup<1, 4>(tr, a, s);
+        launch_gateup<1, 2>(tr, a, s);
     else if (nch <= 2)
-        launch_gateup<2, 4>(tr, a, s);
+        launch_gateup<2, 2>(tr, a, s);
     else if (nch <= 4)
         launch_gateup<4, 2>(tr, a, s);
     else
