@@ -29,6 +29,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 METRIC = "MoE-layer tokens/s, prefill T=4096 & decode T=1; % of MFMA/HBM peak"
@@ -36,6 +37,34 @@ METRIC = "MoE-layer tokens/s, prefill T=4096 & decode T=1; % of MFMA/HBM peak"
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per dispatch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-kernel scaled), or None when there is none
+    or the kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            k = json.load(f)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    from bit_moe_expert_03_amd.profsum import source_hash
+    if source_hash(k["sources"]) != k["source_sha256"]:
+        return None
+    return k["traffic_bytes"]
+
+
+def copy_calibration(mb):
+    """A plain copy kernel of known size (int32 x 1 into a second buffer),
+    run three times so that counter passes can scale FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    src = torch.ones((mb << 20) // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def to_dev(a):
@@ -57,10 +86,10 @@ def make_events(n):
 def gateup_decode_bytes(dims):
     """Algorithmic bytes of the decode gate/up kernel: packed codes + bf16
     scale/bias of gate and up for the k routed and the shared expert, x,
-    the logits row, and the fp32 h it writes."""
+    the logits row, and the bf16 h it writes."""
     per_row = dims.d // 2 + 2 * 2 * (dims.d // dims.G)
     w = 2 * per_row * (dims.k * dims.F + dims.Fs)
-    return w + dims.d * 2 + dims.E * 4 + (dims.k * dims.F + dims.Fs) * 4
+    return w + dims.d * 2 + dims.E * 4 + (dims.k * dims.F + dims.Fs) * 2
 
 
 def decode_layer_bytes(dims):
@@ -162,7 +191,8 @@ def bench_decode(B, wl, args):
         "layer_gbs": decode_layer_bytes(dims) / (sec / args.steps) / 1e9,
         "roofline": {"bound": "hbm", "kernel": "decode_gateup_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_launch": gu_bytes, "avg_launch_ms": gu_ms},
+                     "traffic": measured_traffic("decode_gateup_kernel"), "bytes_per_launch": gu_bytes,
+                     "avg_launch_ms": gu_ms},
     }
     log(f"decode: {value:.0f} tok/s, {out['ms_per_step'] * 1e3:.2f} us/step, gate/up {gu_ms * 1e3:.2f} us "
         f"({achieved:.0f} GB/s), down {per_kernel[1] * 1e3:.2f} us")
@@ -198,7 +228,8 @@ def bench_prefill(B, wl, args):
         "layer_mfma_frac": layer_flops(dims) / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
         "roofline": {"bound": "mfma", "kernel": "moe_gateup_kernel", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFS,
-                     "traffic": None, "flops_per_launch": fl, "avg_launch_ms": gu_ms},
+                     "traffic": measured_traffic("moe_gateup_kernel"), "flops_per_launch": fl,
+                     "avg_launch_ms": gu_ms},
     }
     log(f"prefill: {value / 1e6:.2f} M tok/s, {ms * 1e3:.1f} us/step, kernels "
         + ", ".join(f"{n} {t * 1e3:.1f}us" for n, t in zip(names, per_kernel)))
@@ -250,6 +281,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="first run a plain copy kernel of this many MB (scale for counter passes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -262,6 +295,8 @@ def main():
     from bit_moe_expert_03_amd import workload as wl
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()  # fails loudly if the HIP library is not built
+    if args.copy_calib_mb:
+        copy_calibration(args.copy_calib_mb)
 
     dec, host = bench_decode(B, wl, args)
     pre = c3 = None
