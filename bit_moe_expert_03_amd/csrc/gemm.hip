@@ -231,12 +231,28 @@ __device__ __forceinline__ void interleave_hint()
     }
 }
 
-// One 64-wide K step: B codes of this lane from the wave's LDS buffer, A
-// operands from the A stage; the four 16-wide MFMA sub-steps are software
-// pipelined (decode and A reads of sub-step s+1 under the MFMAs of s).
-template <int MS, int G>
-__device__ __forceinline__ void kstep(const uint8_t *astage, const uint8_t *bwave, const SBPair<G> &sb, int j,
-                                      f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
+// This lane's codes of one K step (16 bytes per half-matrix), read from the
+// wave's slice of the LDS buffer of the step's pair.
+struct StepCodes {
+    uint32_t w0[4], w1[4];
+};
+
+// scale and bias of K step j of a pair for this lane's two columns
+struct StepScales {
+    float s0, b0, s1, b1;
+};
+
+template <int G>
+__device__ __forceinline__ StepScales step_scales(const SBPair<G> &sb, int j)
+{
+    const int h = (threadIdx.x & 63) >> 5;
+    StepScales t;
+    sb_pick<G>(sb.s0, sb.b0, j, h, t.s0, t.b0);
+    sb_pick<G>(sb.s1, sb.b1, j, h, t.s1, t.b1);
+    return t;
+}
+
+__device__ __forceinline__ void read_codes(const uint8_t *bwave, int j, StepCodes &sc)
 {
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, n = lane & 31;
@@ -245,11 +261,34 @@ __device__ __forceinline__ void kstep(const uint8_t *astage, const uint8_t *bwav
     const uint4 q0 = bq[n * (kBRow / 16) + (c ^ ((n >> 2) & 3))];
     const int n1 = 32 + n;
     const uint4 q1 = bq[n1 * (kBRow / 16) + (c ^ ((n1 >> 2) & 3))];
-    float s0, b0, s1, b1;
-    sb_pick<G>(sb.s0, sb.b0, j, h, s0, b0);
-    sb_pick<G>(sb.s1, sb.b1, j, h, s1, b1);
-    const uint32_t w0[4] = {q0.x, q0.y, q0.z, q0.w};
-    const uint32_t w1[4] = {q1.x, q1.y, q1.z, q1.w};
+    sc.w0[0] = q0.x; sc.w0[1] = q0.y; sc.w0[2] = q0.z; sc.w0[3] = q0.w;
+    sc.w1[0] = q1.x; sc.w1[1] = q1.y; sc.w1[2] = q1.z; sc.w1[3] = q1.w;
+}
+
+// The decoded B operands of the first sub-step of a K step.
+struct FirstOps {
+    bf16x8 o0, o1;
+};
+
+__device__ __forceinline__ void decode_first(const StepCodes &sc, const StepScales &t, FirstOps &f)
+{
+    f.o0 = decode_sub(sc.w0[0], t.s0, t.b0);
+    f.o1 = decode_sub(sc.w1[0], t.s1, t.b1);
+}
+
+// One 64-wide K step.  The codes of this step (cur) were read and its first
+// sub-step decoded (first) during the previous step; the four 16-wide MFMA
+// sub-steps are software pipelined (decode and A reads of sub-step s+1 under
+// the MFMAs of s), and under the MFMAs of the last sub-step the codes of the
+// next step are read from LDS (bnext, step jn of its pair) and its first
+// sub-step is decoded, so the next step starts with matrix-core work.
+template <int MS, int G>
+__device__ __forceinline__ void kstep(const uint8_t *astage, const StepCodes &cur, const StepScales &sc,
+                                      const FirstOps &first, const uint8_t *bnext, const SBPair<G> &sbnext, int jn,
+                                      StepCodes &nxt, FirstOps &nfirst, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
+{
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, n = lane & 31;
     // A operand of sub-tile i, sub-step s: row 32 i + n, chunk 4 h + s
     const bf16x8 *aq = reinterpret_cast<const bf16x8 *>(__builtin_assume_aligned(astage, 16));
     auto aread = [&](int i, int s) __attribute__((always_inline)) {
@@ -257,8 +296,8 @@ __device__ __forceinline__ void kstep(const uint8_t *astage, const uint8_t *bwav
         return aq[row * (kARow / 16) + ((4 * h + s) ^ ((row >> 1) & 7))];
     };
     bf16x8 o0[2], o1[2];
-    o0[0] = decode_sub(w0[0], s0, b0);
-    o1[0] = decode_sub(w1[0], s1, b1);
+    o0[0] = first.o0;
+    o1[0] = first.o1;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int cu = s & 1, nx = cu ^ 1;
@@ -266,55 +305,81 @@ __device__ __forceinline__ void kstep(const uint8_t *astage, const uint8_t *bwav
 #pragma unroll
         for (int i = 0; i < MS; ++i) av[i] = aread(i, s);
         if (s < 3) {
-            o0[nx] = decode_sub(w0[s + 1], s0, b0);
-            o1[nx] = decode_sub(w1[s + 1], s1, b1);
+            o0[nx] = decode_sub(cur.w0[s + 1], sc.s0, sc.b0);
+            o1[nx] = decode_sub(cur.w1[s + 1], sc.s1, sc.b1);
+        } else {
+            read_codes(bnext, jn, nxt);
+            decode_first(nxt, step_scales<G>(sbnext, jn), nfirst);
         }
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
             acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], o0[cu], acc0[i], 0, 0, 0);
             acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], o1[cu], acc1[i], 0, 0, 0);
         }
-        if (s < 3) interleave_hint<2 * MS, 0>();
+        interleave_hint<2 * MS, 0>();
     }
 }
 
-// One K step of the main loop.  J = kt & 1 selects the A stage and the step
-// inside the pair, BUF the B buffer of the pair.  Entry: this wave's copies
-// of A(kt) (issued one step ago) and of the pair's codes (issued at the
-// previous pair's first step) must land: at odd steps the copies issued at
-// the pair's first step -- next pair's codes and scales, NB operations --
-// may stay in flight.
-template <int MS, int G, int J, int BUF>
+// LDS objects of one block: two A stages, three B buffers (this wave's
+// slices).  Separate objects, each indexed statically, so that reading one
+// never waits for copies still landing in another.
+struct LdsBufs {
+    uint8_t *a0, *a1, *b0, *b1, *b2;
+    template <int I> __device__ __forceinline__ uint8_t *a() const { return I == 0 ? a0 : a1; }
+    template <int I> __device__ __forceinline__ uint8_t *b() const { return I == 0 ? b0 : I == 1 ? b1 : b2; }
+};
+
+// Pipeline state carried from one K step to the next.
+template <int G>
+struct Carry {
+    SBPair<G> sb, sbn;  // scales of the current pair and of the next one
+    StepCodes codes;    // codes of the next step
+    FirstOps first;     // its decoded first sub-step
+};
+
+// One K step.  ST = kt % 6 fixes J = kt & 1 (A stage, step inside the pair)
+// and PB = (kt / 2) % 3 (B buffer of the pair).  Codes are copied two pairs
+// ahead, A one step ahead, scales one pair ahead (registers).  Entry wait:
+// at J = 1 this wave's copy of A(kt) (issued one step ago, before the copies
+// of pair p+2 and the scale loads of pair p+1: NB operations) must have
+// landed; at J = 0 everything, which includes the codes of pair p+1 that
+// the end of the next step reads.  After the barrier every wave's copies up
+// to there are in LDS: copy A(kt+1); at J = 0 copy pair p+2 into the buffer
+// of pair p-1 (last read one step before this one) and load the scales of
+// pair p+1.
+template <int MS, int G, int ST>
 __device__ __forceinline__ void mainloop_step(int kt, int nk, int npair, const uint16_t *const (&rowp)[MS],
-                                              const BSrc &bsrc, uint8_t *a0, uint8_t *a1, uint8_t *b0,
-                                              uint8_t *b1, const SBPair<G> &sb, SBPair<G> &sbnext,
+                                              const BSrc &bsrc, const LdsBufs &L, Carry<G> &cs,
                                               f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
 {
+    constexpr int J = ST & 1, PB = (ST >> 1) % 3;
     constexpr int NB = 4 + 4 * SBPair<G>::NW;  // copies + scale/bias loads of one pair
     if constexpr (J == 1) wait_vmcnt<NB>(); else wait_vmcnt<0>();
     block_sync();
-    a_dma<MS>(rowp, min(kt + 1, nk - 1), J == 0 ? a1 : a0);
+    a_dma<MS>(rowp, min(kt + 1, nk - 1), L.a<J ^ 1>());
     if constexpr (J == 0) {
-        const int pn = min((kt >> 1) + 1, npair - 1);
-        b_dma(bsrc, pn, BUF == 0 ? b1 : b0);
-        sb_load<G>(sbnext, bsrc, pn);
+        b_dma(bsrc, min((kt >> 1) + 2, npair - 1), L.b<(PB + 2) % 3>());
+        sb_load<G>(cs.sbn, bsrc, min((kt >> 1) + 1, npair - 1));
     }
-    kstep<MS, G>(J == 0 ? a0 : a1, BUF == 0 ? b0 : b1, sb, J, acc0, acc1);
+    // next step: same pair at J = 0, first step of the next pair at J = 1
+    constexpr int PBN = J == 0 ? PB : (PB + 1) % 3;
+    const StepCodes cur = cs.codes;
+    const FirstOps first = cs.first;
+    const StepScales sc = step_scales<G>(cs.sb, J);
+    kstep<MS, G>(L.a<J>(), cur, sc, first, L.b<PBN>(), J == 0 ? cs.sb : cs.sbn, J ^ 1, cs.codes, cs.first, acc0,
+                 acc1);
+    if constexpr (J == 1) cs.sb = cs.sbn;
 }
 
 // Main loop shared by both GEMMs: acc0 += A B0^T, acc1 += A B1^T over K for
-// MS live 32-row sub-tiles.  Per K step: A of the next step and, at a
-// pair's first step, the codes and scales of the next pair are copied while
-// the MFMAs of this step run.  Past the end it re-loads valid steps instead
-// of branching; with K a multiple of 256 the 4-step body has no conditions.
+// MS live 32-row sub-tiles.  The (A stage, B buffer) assignment repeats every
+// 6 steps: the loop body is 6 straight-line steps, and 1 to 5 remaining
+// steps run the same instantiations under conditions.  Past the end, copies
+// re-load valid data instead of branching.
 template <int MS, int G>
 __device__ __forceinline__ void mainloop(const uint16_t *const (&rowp)[MS], int K, const BSrc &bsrc,
-                                         uint8_t *lds_a0, uint8_t *lds_a1, uint8_t *lds_b0,
-                                         uint8_t *lds_b1, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
+                                         const LdsBufs &L, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
 {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    uint8_t *bw0 = lds_b0 + wave * kBWave;
-    uint8_t *bw1 = lds_b1 + wave * kBWave;
     const int nk = K / kKStep;
     const int npair = (nk + 1) >> 1;
 #pragma unroll
@@ -322,25 +387,30 @@ __device__ __forceinline__ void mainloop(const uint16_t *const (&rowp)[MS], int 
 #pragma unroll
         for (int r = 0; r < 16; ++r) { acc0[i][r] = 0.f; acc1[i][r] = 0.f; }
 
-    SBPair<G> sbc, sbn;
-    a_dma<MS>(rowp, 0, lds_a0);
-    b_dma(bsrc, 0, bw0);
-    sb_load<G>(sbc, bsrc, 0);
+    Carry<G> cs;
+    a_dma<MS>(rowp, 0, L.a<0>());
+    b_dma(bsrc, 0, L.b<0>());
+    sb_load<G>(cs.sb, bsrc, 0);
+    b_dma(bsrc, min(1, npair - 1), L.b<1>());
+    wait_vmcnt<0>();
+    block_sync();
+    read_codes(L.b<0>(), 0, cs.codes);
+    decode_first(cs.codes, step_scales<G>(cs.sb, 0), cs.first);
 
     int kt = 0;
-    for (; kt + 3 < nk; kt += 4) {  // pairs 2P (buffer 0) and 2P+1 (buffer 1)
-        mainloop_step<MS, G, 0, 0>(kt, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbc, sbn, acc0, acc1);
-        mainloop_step<MS, G, 1, 0>(kt + 1, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbc, sbn, acc0, acc1);
-        mainloop_step<MS, G, 0, 1>(kt + 2, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbn, sbc, acc0, acc1);
-        mainloop_step<MS, G, 1, 1>(kt + 3, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbn, sbc, acc0, acc1);
+    for (; kt + 5 < nk; kt += 6) {
+        mainloop_step<MS, G, 0>(kt, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 1>(kt + 1, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 2>(kt + 2, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 3>(kt + 3, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 4>(kt + 4, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 5>(kt + 5, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
     }
-    if (kt < nk) {  // 1 to 3 remaining steps (K not a multiple of 256)
-        mainloop_step<MS, G, 0, 0>(kt, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbc, sbn, acc0, acc1);
-        if (kt + 1 < nk)
-            mainloop_step<MS, G, 1, 0>(kt + 1, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbc, sbn, acc0, acc1);
-        if (kt + 2 < nk)
-            mainloop_step<MS, G, 0, 1>(kt + 2, nk, npair, rowp, bsrc, lds_a0, lds_a1, bw0, bw1, sbn, sbc, acc0, acc1);
-    }
+    if (kt < nk) mainloop_step<MS, G, 0>(kt, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+    if (kt + 1 < nk) mainloop_step<MS, G, 1>(kt + 1, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+    if (kt + 2 < nk) mainloop_step<MS, G, 2>(kt + 2, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+    if (kt + 3 < nk) mainloop_step<MS, G, 3>(kt + 3, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+    if (kt + 4 < nk) mainloop_step<MS, G, 4>(kt + 4, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
     wait_vmcnt<0>();  // no copy into LDS outlives the loop
 }
 
@@ -361,9 +431,11 @@ template <int MS, int G>
 __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int rows, int N,
                                             const moe_qmat &mg, const moe_qmat &mu, size_t ebase,
                                             uint16_t *out, bool routed, int nt, uint8_t *lds_a0,
-                                            uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1)
+                                            uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1, uint8_t *lds_b2)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wslice = __builtin_amdgcn_readfirstlane(wave) * kBWave;
+    const LdsBufs L = {lds_a0, lds_a1, lds_b0 + wslice, lds_b1 + wslice, lds_b2 + wslice};
     const uint16_t *rowp[MS];
     a_rows<MS>(rowp, a.x, a.d, routed ? a.perm : nullptr, a.k, row0, rows);
     const int ncol0 = nt * 128 + 32 * wave;  // first h column of this wave
@@ -382,7 +454,7 @@ __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int r
     src.kbytes = Kq;
     src.ngroups = Kg;
     f32x16 accg[MS], accu[MS];
-    mainloop<MS, G>(rowp, a.d, src, lds_a0, lds_a1, lds_b0, lds_b1, accg, accu);
+    mainloop<MS, G>(rowp, a.d, src, L, accg, accu);
     // epilogue: h = bf16(silu(g) * u) into an LDS tile [MS*32 rows][128 cols]
     // (rows 0..63 in lds_b0, 64..127 in lds_b1, 256-byte rows), then 16-byte
     // coalesced stores of whole 256-byte row segments
@@ -417,6 +489,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gateup_kernel(GateUpArgs 
     __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[BM * kARow];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kBBuf];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_b2[kBBuf];
     const int L = xcd_logical_block(blockIdx.x, a.nblk_pad);
     int row0, rows, N, nt;
     const moe_qmat *mg, *mu;
@@ -448,24 +521,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gateup_kernel(GateUpArgs 
     }
     const int msub = (rows + 31) >> 5;  // live 32-row sub-tiles (block-uniform)
     if (BM >= 128 && msub > 2)
-        gateup_body<(BM >= 128 ? 4 : 1), G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+        gateup_body<(BM >= 128 ? 4 : 1), G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
     else if (BM >= 64 && msub == 2)
-        gateup_body<(BM >= 64 ? 2 : 1), G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+        gateup_body<(BM >= 64 ? 2 : 1), G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
     else
-        gateup_body<1, G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1);
+        gateup_body<1, G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
 }
 
 template <int MS, int G>
 __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows, int K,
                                           const moe_qmat &m, size_t ebase, const uint16_t *hsrc,
                                           int orow0, bool routed, int nt, uint8_t *lds_a0,
-                                          uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1,
-                                          float *row_w)
+                                          uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1, uint8_t *lds_b2)
 {
-    // routing weight of every routed row of the tile (read in the epilogue)
-    if (routed && threadIdx.x < MS * 32)
-        row_w[threadIdx.x] = a.topk_w[a.perm[row0 + min((int)threadIdx.x, rows - 1)]];
+    // routing weight of routed row tid of the tile; staged into LDS for the
+    // epilogue once the main loop has freed the third B buffer
+    float wrow = 1.0f;
+    if (routed && threadIdx.x < MS * 32) wrow = a.topk_w[a.perm[row0 + min((int)threadIdx.x, rows - 1)]];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wslice = __builtin_amdgcn_readfirstlane(wave) * kBWave;
+    const LdsBufs L = {lds_a0, lds_a1, lds_b0 + wslice, lds_b1 + wslice, lds_b2 + wslice};
     const uint16_t *rowp[MS];
     a_rows<MS>(rowp, hsrc, K, nullptr, 1, row0, rows);
     const int ncol0 = nt * 256 + 64 * wave;  // this wave: columns [ncol0, ncol0 + 64)
@@ -483,10 +558,13 @@ __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows,
     src.kbytes = Kq;
     src.ngroups = Kg;
     f32x16 acc0[MS], acc1[MS];
-    mainloop<MS, G>(rowp, K, src, lds_a0, lds_a1, lds_b0, lds_b1, acc0, acc1);
+    mainloop<MS, G>(rowp, K, src, L, acc0, acc1);
     // epilogue: o = w_route * acc as bf16 into an LDS tile [MS*32 rows][256
-    // cols] (512-byte rows; rows 32 q .. 32 q + 31 in the q-th of the four
-    // LDS objects), then 16-byte coalesced stores of 512-byte row segments
+    // cols] (512-byte rows; rows 32 q .. 32 q + 31 in the q-th of four LDS
+    // objects), then 16-byte coalesced stores of 512-byte row segments
+    block_sync();
+    float *row_w = reinterpret_cast<float *>(lds_b2);
+    if (threadIdx.x < MS * 32) row_w[threadIdx.x] = wrow;
     block_sync();
     const int half = lane >> 5;
     const int n = lane & 31;
@@ -521,7 +599,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[BM * kARow];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kBBuf];
-    __shared__ float row_w[kMaxMS * 32];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_b2[kBBuf];
     const int L = xcd_logical_block(blockIdx.x, a.nblk_pad);
     int row0, rows, K, nt;
     const moe_qmat *m;
@@ -553,11 +631,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     }
     const int msub = (rows + 31) >> 5;
     if (BM >= 128 && msub > 2)
-        down_body<(BM >= 128 ? 4 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, row_w);
+        down_body<(BM >= 128 ? 4 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
     else if (BM >= 64 && msub == 2)
-        down_body<(BM >= 64 ? 2 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, row_w);
+        down_body<(BM >= 64 ? 2 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
     else
-        down_body<1, G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, row_w);
+        down_body<1, G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
 }
 
 // one wave per token: 16-byte loads of the k routed rows and the shared row
