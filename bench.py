@@ -54,6 +54,50 @@ def measured_traffic(kernel):
     return k["traffic_bytes"]
 
 
+def achievable_peaks():
+    """Context for the roofline fractions: what library code reaches on this
+    box -- a device-to-device copy of 1 GiB (bytes read + written per
+    second) and a 8192^3 bf16 matrix product on contiguous operands."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        dst.copy_(src)
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    for _ in range(10):
+        c = a @ b
+    e2.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) / 1e3 / 10
+    mm_s = e1.elapsed_time(e2) / 1e3 / 10
+    out = {"hbm_copy_gbs": 2 * src.numel() * 4 / copy_s / 1e9, "bf16_matmul_tflops": 2 * 8192 ** 3 / mm_s / 1e12,
+           "how": "torch copy_ of 1 GiB (read + write) and torch bf16 8192^3 matmul, 10 reps each"}
+    del src, dst, a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs visible"
+
+
 def copy_calibration(mb):
     """A plain copy kernel of known size (int32 x 1 into a second buffer),
     run three times so that counter passes can scale FETCH_SIZE/WRITE_SIZE."""
@@ -140,10 +184,13 @@ def run_timed(B, dm, calls, steps, warmup):
     torch.cuda.synchronize()
     g.replay()  # untimed: the first replay uploads the graph
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    reps = []
+    for _ in range(3):  # median of three timed replays
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        reps.append(time.perf_counter() - t0)
+    reps.sort()
     evs = [make_events(2 * nk) for _ in range(steps)]
     with torch.cuda.stream(stream):
         for i in range(steps):
@@ -151,7 +198,7 @@ def run_timed(B, dm, calls, steps, warmup):
             B.moe_layer_timed(dm, lg, x, w, r, y, ws, [e.cuda_event for e in evs[i]], stream=stream)
     torch.cuda.synchronize()
     per_kernel = [sum(ev[2 * j].elapsed_time(ev[2 * j + 1]) for ev in evs) / steps for j in range(nk)]
-    return t1 - t0, per_kernel
+    return reps[1], per_kernel
 
 
 def bench_decode(B, wl, args):
@@ -224,6 +271,7 @@ def bench_prefill(B, wl, args):
         "config": {"workload": "prefill T=4096 Zipf(1)-skewed routing, d=2048, E=256, top-8 + shared, "
                                "F=Fs=512, int4 G=64, one weight set", "T": dims.T},
         "per_kernel_ms": dict(zip(names, per_kernel)),
+        "routing_gbs": (dims.T * dims.E * 4 + dims.T * dims.k * 16) / (sum(per_kernel[:3]) * 1e-3) / 1e9,
         "layer_tflops": layer_flops(dims) / (ms * 1e-3) / 1e12,
         "layer_mfma_frac": layer_flops(dims) / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
         "roofline": {"bound": "mfma", "kernel": "moe_gateup_kernel", "achieved": achieved,
@@ -249,7 +297,7 @@ def cpu_baseline_decode(wl, host, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle", "host": host_cpu(),
             "sample": f"{n} decode steps (T=1, route + fp64 FFN), 2 weight sets held in host memory; "
                       "one token per call, so the oracle's token loop runs on one thread"}
 
@@ -267,7 +315,7 @@ def cpu_baseline_prefill(wl, c, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or ntok + n > dims.T:
             break
-    return {"value": ntok / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+    return {"value": ntok / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle", "host": host_cpu(),
             "sample": f"routing of all {dims.T} tokens + fp64 FFN of the first {ntok} tokens of the "
                       "T=4096 Zipf workload (OpenMP over tokens)"}
 
@@ -298,10 +346,14 @@ def main():
     if args.copy_calib_mb:
         copy_calibration(args.copy_calib_mb)
 
+    peaks = achievable_peaks()
+    log(f"achievable: copy {peaks['hbm_copy_gbs']:.0f} GB/s, bf16 matmul {peaks['bf16_matmul_tflops']:.0f} TFLOP/s")
     dec, host = bench_decode(B, wl, args)
+    dec["roofline"]["frac_of_achievable"] = dec["roofline"]["achieved"] / peaks["hbm_copy_gbs"]
     pre = c3 = None
     if not args.no_prefill:
         pre, c3 = bench_prefill(B, wl, args)
+        pre["roofline"]["frac_of_achievable"] = pre["roofline"]["achieved"] / peaks["bf16_matmul_tflops"]
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -327,6 +379,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_detail": {k: dec[k] for k in ("per_kernel_ms", "layer_bytes", "layer_gbs")},
         "prefill": pre,
+        "achievable": peaks,
     }
     print(json.dumps(line), flush=True)
 

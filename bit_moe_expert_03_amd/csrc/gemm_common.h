@@ -1,0 +1,113 @@
+// Pieces shared by the grouped-GEMM kernels of the prefill path (gfx950):
+// kernel arguments, XCD-aware block order, explicit memory-counter waits, the
+// fence-free workgroup barrier, scale/bias words of a pair of K steps and the
+// register decode of eight 4-bit codes into a bf16 MFMA operand.
+#pragma once
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kKStep = 64;             // contraction per main-loop step
+
+struct GemmTiles {
+    const int32_t *tile_expert, *tile_row0, *tile_rows, *num_tiles;
+    int max_tiles;
+};
+
+struct GateUpArgs {
+    const uint16_t *x;      // [T][d]
+    const int32_t *perm;    // [T*k]
+    int T, d, k, G, F, Fs;
+    moe_qmat gate, up, sgate, sup;
+    GemmTiles tiles;
+    int ntn_r, ntn_s;       // 128-column blocks per tile (routed, shared)
+    int nblk_r, nblk_s;     // blocks of the routed and the shared part
+    int nblk_pad;           // grid size (multiple of 8)
+    uint16_t *h_r;          // [T*k][F] sorted rows
+    uint16_t *h_s;          // [T][Fs]
+};
+
+struct DownArgs {
+    const uint16_t *h_r, *h_s;
+    const int32_t *perm;
+    const float *topk_w;
+    int T, d, k, G, F, Fs;
+    moe_qmat down, sdown;
+    GemmTiles tiles;
+    int ntn;                // 256-column blocks (d / 256, rounded up)
+    int nblk_r, nblk_s, nblk_pad;
+    uint16_t *obuf;         // [T*k + T][d] weighted outputs: sorted routed rows, then shared
+};
+
+// Blocks are dispatched round-robin over the 8 XCDs; renumber them so that
+// consecutive logical blocks (the column blocks of one tile, then the next
+// tile of the same expert) run on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk_pad)
+{
+    const int per = nblk_pad >> 3;
+    return (bid & 7) * per + (bid >> 3);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Workgroup barrier without a memory fence: a fence would also wait for the
+// global->LDS copies of later steps; every wave waits for its own copies of
+// the current step (wait_vmcnt) before arriving, so after the barrier the
+// whole step is in LDS.
+__device__ __forceinline__ void block_sync()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
+// scale/bias words of one pair for the lane's two rows (NW words of two
+// bf16 each; group order = pair's groups in ascending order)
+template <int G>
+struct SBPair {
+    static constexpr int NW = G == 32 ? 2 : 1;
+    uint32_t s0[NW], b0[NW], s1[NW], b1[NW];
+};
+
+// scale (low 16 bits of the result) and bias of K step j of the pair, half h
+template <int G>
+__device__ __forceinline__ void sb_pick(const uint32_t (&s)[SBPair<G>::NW], const uint32_t (&b)[SBPair<G>::NW],
+                                        int j, int h, float &sf, float &bf)
+{
+    const int gi = (64 * j + 32 * h) / G;  // group index inside the pair
+    const uint32_t sw = s[gi >> 1 < SBPair<G>::NW ? gi >> 1 : 0];
+    const uint32_t bw = b[gi >> 1 < SBPair<G>::NW ? gi >> 1 : 0];
+    const int sh = (gi & 1) * 16;
+    sf = __uint_as_float((sw >> sh) << 16);
+    bf = __uint_as_float((bw >> sh) << 16);
+}
+
+__device__ __forceinline__ bf16x8 decode_sub(uint32_t w, float s, float b)
+{
+    uint32_t o[4];
+    dequant8_bf16(w, s, b, o);
+    return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// scheduling hint: interleave n MFMAs with the decode VALU and LDS reads of
+// the next sub-step (6 VALU ops fit under one 32x32x16 MFMA)
+template <int NMFMA, int NDS>
+__device__ __forceinline__ void interleave_hint()
+{
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
+    }
+}
+
+}  // namespace moe

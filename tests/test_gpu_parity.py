@@ -26,6 +26,10 @@ SMALL = {
     "T2_smallest_gemm": (wl.Dims(T=2, d=128, E=8, k=2, F=64, Fs=64, G=32), False),
     "zipf_T500_E64_k6": (wl.Dims(T=500, d=128, E=64, k=6, F=64, Fs=64, G=32), True),
     "T1_small_decode": (wl.Dims(T=1, d=256, E=16, k=4, F=128, Fs=192, G=64), False),
+    # many rows per expert: pairs of full 128-row tiles (256-row super-tiles),
+    # widths that are not multiples of 128 and odd K-step counts
+    "T1000_E4_k2_pairs": (wl.Dims(T=1000, d=128, E=4, k=2, F=192, Fs=64, G=64), False),
+    "T600_E2_k1_G128_pairs": (wl.Dims(T=600, d=256, E=2, k=1, F=128, Fs=128, G=128), False),
 }
 
 
@@ -120,6 +124,15 @@ def test_layer_small_shapes_all_tokens(name):
         g = run(c, mode=mode)
         ref = check_routing(c, g)
         check_y(c, g, ref)
+
+
+@pytest.mark.parametrize("name", [n for n in SMALL if SMALL[n][0].T >= 2])
+def test_layer_small_shapes_tile128(name):
+    """Every small shape with 128-row tiles (the 256-row super-tile kernels)."""
+    c = _case(name)
+    g = run(c, tile_m=128)
+    ref = check_routing(c, g)
+    check_y(c, g, ref)
 
 
 def test_layer_tiny_config_all_tokens():
