@@ -51,6 +51,11 @@ moe_status make_plan(const moe_dims *dm, Plan *p, const char **why)
     if (!mult_ok(d.d, d.G)) { *why = "d must be a positive multiple of 64 and of G, <= 16384"; return MOE_ERR_SHAPE; }
     if (!mult_ok(d.F, d.G)) { *why = "F must be a positive multiple of 64 and of G, <= 16384"; return MOE_ERR_SHAPE; }
     if (!mult_ok(d.Fs, d.G)) { *why = "Fs must be a positive multiple of 64 and of G, <= 16384"; return MOE_ERR_SHAPE; }
+    if ((int64_t)d.T * d.d >= ((int64_t)1 << 31) || (int64_t)d.T * d.k * d.F >= ((int64_t)1 << 31) ||
+        (int64_t)d.T * d.Fs >= ((int64_t)1 << 31)) {
+        *why = "T*d, T*k*F and T*Fs must each be below 2^31";
+        return MOE_ERR_SHAPE;
+    }
     if (d.tile_m != 0 && d.tile_m != 32 && d.tile_m != 64 && d.tile_m != 128) {
         *why = "tile_m not in {0, 32, 64, 128}";
         return MOE_ERR_SHAPE;

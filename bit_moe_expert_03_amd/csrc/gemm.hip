@@ -57,49 +57,59 @@ constexpr int kBRow = 64;                         // bytes of codes per B row pe
 constexpr int kBWave = 64 * kBRow;                // 4 KB per wave
 constexpr int kBBuf = 4 * kBWave;                 // 16 KB per buffer
 
+// One 16-byte-per-lane global->LDS copy (global_load_lds_dwordx4, LDS base in
+// M0) from base + voff: a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset, so a row address costs one VGPR instead of two.
+// Issued from inline assembly so that the compiler does not treat LDS reads
+// of the other buffers as dependent on it (it would wait for every copy in
+// flight before each of them); the main loop counts these copies itself
+// (wait_vmcnt) and fences them with the barrier.  The s_nop covers both the
+// M0 write and a base just moved into SGPRs by a VALU readfirstlane.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint8_t *lds)
+{
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds);
+    const uint64_t sb = uniform_u64((uint64_t)(uintptr_t)base);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(sb)
+                 : "memory", "m0");
+}
+
 // Copy the A tile of K step kt (MS*32 rows x 64 bf16) into an A stage:
 // wave w, copy i moves rows 8 (4 i + w) .. +7, 8 lanes per 128-byte row.
-// rowp[i] is this lane's source row of copy i (rows past the tile's end
-// point at a valid row; their products land in discarded output rows).
+// aoff[i] is this lane's byte offset (source row, chunk) from abase for copy
+// i (rows past the tile's end point at a valid row; their products land in
+// discarded output rows).
 template <int MS>
-__device__ __forceinline__ void a_dma(const uint16_t *const (&rowp)[MS], int kt, uint8_t *stage)
+__device__ __forceinline__ void a_dma(const uint16_t *abase, const uint32_t (&aoff)[MS], int kt, uint8_t *stage)
 {
-    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slot = lane & 7;
+    const uint16_t *base = abase + kt * kKStep;
 #pragma unroll
-    for (int i = 0; i < MS; ++i) {
-        const int row = 8 * (4 * i + wave) + (lane >> 3);
-        const int c = slot ^ ((row >> 1) & 7);  // source chunk stored in this slot
-        __builtin_amdgcn_global_load_lds((const void *)(rowp[i] + kt * kKStep + c * 8),
-                                         (lds_void_t *)(stage + (4 * i + wave) * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < MS; ++i) dma16(base, aoff[i], stage + (4 * i + wave) * 1024);
 }
 
 // Per-wave B source: the 64 rows this wave multiplies (rows 0..31 feed the
-// first accumulator set, 32..63 the second) and their scale/bias rows.
+// first accumulator set, 32..63 the second) and their scale/bias rows, as
+// wave-uniform bases plus per-lane byte offsets.
 struct BSrc {
-    const uint8_t *q[4];   // code row of the 16-row group this lane copies in DMA step q
-    const uint16_t *s0, *b0, *s1, *b1;  // scale/bias rows of this lane's two MFMA columns
+    const uint8_t *q[4];   // code row 16 q of this wave (copy q moves rows 16 q .. 16 q + 15)
+    uint32_t qrow;         // this lane's row inside a copy (lane / 4) times the row pitch
+    uint32_t c16;          // byte offset of the source chunk stored in this lane's slot
+    const uint16_t *s0, *b0, *s1, *b1;  // scale/bias rows 0 (first set) and 32 (second set)
+    uint32_t soff;         // byte offset of this lane's scale/bias row (lane % 32)
     int kbytes;            // bytes of codes per row (K / 2)
     int ngroups;           // groups per row (K / G)
 };
 
 // Copy the codes of pair p (K steps 2p, 2p+1: 64 bytes per row) of this
-// wave's 64 rows into its slice of an LDS buffer: 4 copies of 16 rows x 64 B.
+// wave's 64 rows into its slice of an LDS buffer: 4 copies of 16 rows x 64 B;
+// chunk c of row r lands in slot c ^ ((r >> 2) & 3) (src.c16 holds the chunk
+// of this lane's slot).  In the half pair at the end of an odd step count the
+// window is clamped to the row.
 __device__ __forceinline__ void b_dma(const BSrc &src, int p, uint8_t *wave_buf)
 {
-    const int lane = threadIdx.x & 63;
-    const int sub = lane >> 2;          // row within the 16-row group
-    const int slot = lane & 3;          // destination chunk slot
+    const uint32_t off = src.qrow + min(64u * p + src.c16, (uint32_t)src.kbytes - 16u);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = 16 * q + sub;
-        const int c = slot ^ ((r >> 2) & 3);  // source chunk stored in this slot
-        const int off = min(64 * p + 16 * c, src.kbytes - 16);
-        __builtin_amdgcn_global_load_lds((const void *)(src.q[q] + off), (lds_void_t *)(wave_buf + q * 1024), 16, 0,
-                                         0);
-    }
+    for (int q = 0; q < 4; ++q) dma16(src.q[q], off, wave_buf + q * 1024);
 }
 
 template <int G>
@@ -107,22 +117,29 @@ __device__ __forceinline__ void sb_load(SBPair<G> &t, const BSrc &src, int p)
 {
     constexpr int NG = 128 / G;  // groups per pair
     const int g0 = p * NG;
+    auto at = [&](const uint16_t *base, int g) __attribute__((always_inline)) {
+        return reinterpret_cast<const uint8_t *>(base) + src.soff + 2 * g;
+    };
     if constexpr (G == 128) {
-        t.s0[0] = src.s0[g0]; t.b0[0] = src.b0[g0];
-        t.s1[0] = src.s1[g0]; t.b1[0] = src.b1[g0];
+        t.s0[0] = *reinterpret_cast<const uint16_t *>(at(src.s0, g0));
+        t.b0[0] = *reinterpret_cast<const uint16_t *>(at(src.b0, g0));
+        t.s1[0] = *reinterpret_cast<const uint16_t *>(at(src.s1, g0));
+        t.b1[0] = *reinterpret_cast<const uint16_t *>(at(src.b1, g0));
     } else {
 #pragma unroll
         for (int w = 0; w < SBPair<G>::NW; ++w) {
             const int g = g0 + 2 * w;
             if (g + 1 < src.ngroups) {  // both groups of the word exist: one 4-byte load
-                t.s0[w] = *reinterpret_cast<const uint32_t *>(src.s0 + g);
-                t.b0[w] = *reinterpret_cast<const uint32_t *>(src.b0 + g);
-                t.s1[w] = *reinterpret_cast<const uint32_t *>(src.s1 + g);
-                t.b1[w] = *reinterpret_cast<const uint32_t *>(src.b1 + g);
+                t.s0[w] = *reinterpret_cast<const uint32_t *>(at(src.s0, g));
+                t.b0[w] = *reinterpret_cast<const uint32_t *>(at(src.b0, g));
+                t.s1[w] = *reinterpret_cast<const uint32_t *>(at(src.s1, g));
+                t.b1[w] = *reinterpret_cast<const uint32_t *>(at(src.b1, g));
             } else {  // tail of a row with an odd group count
                 const int gg = min(g, src.ngroups - 1);
-                t.s0[w] = src.s0[gg]; t.b0[w] = src.b0[gg];
-                t.s1[w] = src.s1[gg]; t.b1[w] = src.b1[gg];
+                t.s0[w] = *reinterpret_cast<const uint16_t *>(at(src.s0, gg));
+                t.b0[w] = *reinterpret_cast<const uint16_t *>(at(src.b0, gg));
+                t.s1[w] = *reinterpret_cast<const uint16_t *>(at(src.s1, gg));
+                t.b1[w] = *reinterpret_cast<const uint16_t *>(at(src.b1, gg));
             }
         }
     }
@@ -181,7 +198,7 @@ __device__ __forceinline__ void decode_first(const StepCodes &sc, const StepScal
 // sub-step is decoded, so the next step starts with matrix-core work.
 template <int MS, int G>
 __device__ __forceinline__ void kstep(const uint8_t *astage, const StepCodes &cur, const StepScales &sc,
-                                      const FirstOps &first, const uint8_t *bnext, const SBPair<G> &sbnext, int jn,
+                                      const FirstOps &first, const uint8_t *bnext, SBPair<G> &sbnext, int jn,
                                       StepCodes &nxt, FirstOps &nfirst, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
 {
     const int lane = threadIdx.x & 63;
@@ -206,6 +223,11 @@ __device__ __forceinline__ void kstep(const uint8_t *astage, const StepCodes &cu
             o1[nx] = decode_sub(cur.w1[s + 1], sc.s1, sc.b1);
         } else {
             read_codes(bnext, jn, nxt);
+            // the next pair's scales are consumed here and not earlier: their
+            // loads may still be in flight before this point
+#pragma unroll
+            for (int w = 0; w < SBPair<G>::NW; ++w)
+                asm volatile("" : "+v"(sbnext.s0[w]), "+v"(sbnext.b0[w]), "+v"(sbnext.s1[w]), "+v"(sbnext.b1[w]));
             decode_first(nxt, step_scales<G>(sbnext, jn), nfirst);
         }
 #pragma unroll
@@ -236,28 +258,25 @@ struct Carry {
 
 // One K step.  ST = kt % 6 fixes J = kt & 1 (A stage, step inside the pair)
 // and PB = (kt / 2) % 3 (B buffer of the pair).  Codes are copied two pairs
-// ahead, A one step ahead, scales one pair ahead (registers).  Entry wait:
-// at J = 1 this wave's copy of A(kt) (issued one step ago, before the copies
-// of pair p+2 and the scale loads of pair p+1: NB operations) must have
-// landed; at J = 0 everything, which includes the codes of pair p+1 that
-// the end of the next step reads.  After the barrier every wave's copies up
-// to there are in LDS: copy A(kt+1); at J = 0 copy pair p+2 into the buffer
-// of pair p-1 (last read one step before this one) and load the scales of
-// pair p+1.
+// ahead, A one step ahead, scales one pair ahead (registers).  Issue order
+// at J = 0: the scale loads of pair p+1, the copies of A(kt+1), then those
+// of pair p+2 (into the buffer of pair p-1, last read one step before this
+// one); at J = 1 the copies of A(kt+1).  Entry wait: at J = 1 the scales and
+// this wave's copy of A(kt) must have landed, the 4 code copies issued after
+// them need not; at J = 0 everything, which includes the codes of pair p+1
+// that the end of the next step reads.  After the barrier every wave's
+// copies up to there are in LDS.
 template <int MS, int G, int ST>
-__device__ __forceinline__ void mainloop_step(int kt, int nk, int npair, const uint16_t *const (&rowp)[MS],
-                                              const BSrc &bsrc, const LdsBufs &L, Carry<G> &cs,
-                                              f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
+__device__ __forceinline__ void mainloop_step(int kt, int nk, int npair, const uint16_t *abase,
+                                              const uint32_t (&aoff)[MS], const BSrc &bsrc, const LdsBufs &L,
+                                              Carry<G> &cs, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
 {
     constexpr int J = ST & 1, PB = (ST >> 1) % 3;
-    constexpr int NB = 4 + 4 * SBPair<G>::NW;  // copies + scale/bias loads of one pair
-    if constexpr (J == 1) wait_vmcnt<NB>(); else wait_vmcnt<0>();
+    if constexpr (J == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
     block_sync();
-    a_dma<MS>(rowp, min(kt + 1, nk - 1), L.a<J ^ 1>());
-    if constexpr (J == 0) {
-        b_dma(bsrc, min((kt >> 1) + 2, npair - 1), L.b<(PB + 2) % 3>());
-        sb_load<G>(cs.sbn, bsrc, min((kt >> 1) + 1, npair - 1));
-    }
+    if constexpr (J == 0) sb_load<G>(cs.sbn, bsrc, min((kt >> 1) + 1, npair - 1));
+    a_dma<MS>(abase, aoff, min(kt + 1, nk - 1), L.a<J ^ 1>());
+    if constexpr (J == 0) b_dma(bsrc, min((kt >> 1) + 2, npair - 1), L.b<(PB + 2) % 3>());
     // next step: same pair at J = 0, first step of the next pair at J = 1
     constexpr int PBN = J == 0 ? PB : (PB + 1) % 3;
     const StepCodes cur = cs.codes;
@@ -274,7 +293,7 @@ __device__ __forceinline__ void mainloop_step(int kt, int nk, int npair, const u
 // steps run the same instantiations under conditions.  Past the end, copies
 // re-load valid data instead of branching.
 template <int MS, int G>
-__device__ __forceinline__ void mainloop(const uint16_t *const (&rowp)[MS], int K, const BSrc &bsrc,
+__device__ __forceinline__ void mainloop(const uint16_t *abase, const uint32_t (&aoff)[MS], int K, const BSrc &bsrc,
                                          const LdsBufs &L, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
 {
     const int nk = K / kKStep;
@@ -285,9 +304,9 @@ __device__ __forceinline__ void mainloop(const uint16_t *const (&rowp)[MS], int 
         for (int r = 0; r < 16; ++r) { acc0[i][r] = 0.f; acc1[i][r] = 0.f; }
 
     Carry<G> cs;
-    a_dma<MS>(rowp, 0, L.a<0>());
-    b_dma(bsrc, 0, L.b<0>());
     sb_load<G>(cs.sb, bsrc, 0);
+    a_dma<MS>(abase, aoff, 0, L.a<0>());
+    b_dma(bsrc, 0, L.b<0>());
     b_dma(bsrc, min(1, npair - 1), L.b<1>());
     wait_vmcnt<0>();
     block_sync();
@@ -296,31 +315,39 @@ __device__ __forceinline__ void mainloop(const uint16_t *const (&rowp)[MS], int 
 
     int kt = 0;
     for (; kt + 5 < nk; kt += 6) {
-        mainloop_step<MS, G, 0>(kt, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
-        mainloop_step<MS, G, 1>(kt + 1, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
-        mainloop_step<MS, G, 2>(kt + 2, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
-        mainloop_step<MS, G, 3>(kt + 3, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
-        mainloop_step<MS, G, 4>(kt + 4, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
-        mainloop_step<MS, G, 5>(kt + 5, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 0>(kt, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 1>(kt + 1, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 2>(kt + 2, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 3>(kt + 3, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 4>(kt + 4, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 5>(kt + 5, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
     }
-    if (kt < nk) mainloop_step<MS, G, 0>(kt, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
-    if (kt + 1 < nk) mainloop_step<MS, G, 1>(kt + 1, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
-    if (kt + 2 < nk) mainloop_step<MS, G, 2>(kt + 2, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
-    if (kt + 3 < nk) mainloop_step<MS, G, 3>(kt + 3, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
-    if (kt + 4 < nk) mainloop_step<MS, G, 4>(kt + 4, nk, npair, rowp, bsrc, L, cs, acc0, acc1);
+    if (kt < nk) mainloop_step<MS, G, 0>(kt, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+    if (kt + 1 < nk) mainloop_step<MS, G, 1>(kt + 1, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+    if (kt + 2 < nk) mainloop_step<MS, G, 2>(kt + 2, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+    if (kt + 3 < nk) mainloop_step<MS, G, 3>(kt + 3, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+    if (kt + 4 < nk) mainloop_step<MS, G, 4>(kt + 4, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
     wait_vmcnt<0>();  // no copy into LDS outlives the loop
 }
 
-// gathered / contiguous A rows of one tile for sub-tiles < MS
+// Byte offsets from the A base of this lane's source (row, chunk) for the A
+// copies of sub-tiles < MS: copy i fills rows 8 (4 i + w) + lane / 8 of the
+// stage, 8 lanes per 128-byte row, and the lane in slot c of its row copies
+// chunk c ^ ((row >> 1) & 7).  Rows are gathered through perm (routed tiles)
+// or contiguous; rows past the tile's end repeat its last row.
 template <int MS>
-__device__ __forceinline__ void a_rows(const uint16_t *(&rowp)[MS], const uint16_t *base, int ld,
-                                       const int32_t *perm, int k, int row0, int rows)
+__device__ __forceinline__ void a_offsets(uint32_t (&aoff)[MS], int ld, const int32_t *perm, int k, int row0,
+                                          int rows)
 {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
-        const int m = min((int)(threadIdx.x >> 3) + i * (kGemmThreads / 8), rows - 1);
+        const int row = 8 * (4 * i + wave) + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        const int m = min(row, rows - 1);
         const int src = perm ? perm[row0 + m] / k : row0 + m;
-        rowp[i] = base + (size_t)src * ld;
+        aoff[i] = (uint32_t)src * (uint32_t)ld * 2u + (uint32_t)c * 16u;
     }
 }
 
@@ -330,28 +357,29 @@ __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int r
                                             uint16_t *out, bool routed, int nt, uint8_t *lds_a0,
                                             uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1, uint8_t *lds_b2)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wslice = __builtin_amdgcn_readfirstlane(wave) * kBWave;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wslice = wave * kBWave;
     const LdsBufs L = {lds_a0, lds_a1, lds_b0 + wslice, lds_b1 + wslice, lds_b2 + wslice};
-    const uint16_t *rowp[MS];
-    a_rows<MS>(rowp, a.x, a.d, routed ? a.perm : nullptr, a.k, row0, rows);
+    uint32_t aoff[MS];
+    a_offsets<MS>(aoff, a.d, routed ? a.perm : nullptr, a.k, row0, rows);
     const int ncol0 = nt * 128 + 32 * wave;  // first h column of this wave
     const int nbase = ncol0 < N ? ncol0 : 0;  // idle waves compute on valid rows
     const int Kq = a.d >> 1, Kg = a.d / G;
     BSrc src;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {  // DMA rows 16q + lane/4: q < 2 gate, q >= 2 up
-        const int r = 16 * q + (lane >> 2);
-        const moe_qmat &m = q < 2 ? mg : mu;
-        src.q[q] = m.q + (ebase + nbase + (r & 31)) * Kq;
-    }
-    const size_t brow = ebase + nbase + (lane & 31);
-    src.s0 = mg.s + brow * Kg; src.b0 = mg.b + brow * Kg;
-    src.s1 = mu.s + brow * Kg; src.b1 = mu.b + brow * Kg;
+    for (int q = 0; q < 4; ++q)  // copy q moves rows 16 q ..: q < 2 gate, q >= 2 up
+        src.q[q] = (q < 2 ? mg : mu).q + uniform_size((ebase + nbase + 16 * (q & 1)) * Kq);
+    src.qrow = (uint32_t)(lane >> 2) * Kq;
+    src.c16 = 16u * ((lane & 3) ^ ((lane >> 4) & 3));
+    const size_t boff = uniform_size((ebase + nbase) * Kg);
+    src.s0 = mg.s + boff; src.b0 = mg.b + boff;
+    src.s1 = mu.s + boff; src.b1 = mu.b + boff;
+    src.soff = (uint32_t)(lane & 31) * Kg * 2u;
     src.kbytes = Kq;
     src.ngroups = Kg;
     f32x16 accg[MS], accu[MS];
-    mainloop<MS, G>(rowp, a.d, src, L, accg, accu);
+    mainloop<MS, G>(a.x, aoff, a.d, src, L, accg, accu);
     // epilogue: h = bf16(silu(g) * u) into an LDS tile [MS*32 rows][128 cols]
     // (rows 0..63 in lds_b0, 64..127 in lds_b1, 256-byte rows), then 16-byte
     // coalesced stores of whole 256-byte row segments
@@ -435,27 +463,28 @@ __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows,
     // epilogue once the main loop has freed the third B buffer
     float wrow = 1.0f;
     if (routed && threadIdx.x < MS * 32) wrow = a.topk_w[a.perm[row0 + min((int)threadIdx.x, rows - 1)]];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wslice = __builtin_amdgcn_readfirstlane(wave) * kBWave;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wslice = wave * kBWave;
     const LdsBufs L = {lds_a0, lds_a1, lds_b0 + wslice, lds_b1 + wslice, lds_b2 + wslice};
-    const uint16_t *rowp[MS];
-    a_rows<MS>(rowp, hsrc, K, nullptr, 1, row0, rows);
+    uint32_t aoff[MS];
+    a_offsets<MS>(aoff, K, nullptr, 1, row0, rows);
     const int ncol0 = nt * 256 + 64 * wave;  // this wave: columns [ncol0, ncol0 + 64)
     const int nbase = ncol0 < a.d ? ncol0 : 0;  // idle waves compute on valid rows
     const int Kq = K >> 1, Kg = K / G;
     BSrc src;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = 16 * q + (lane >> 2);
-        src.q[q] = m.q + (ebase + nbase + r) * Kq;
-    }
-    const size_t r0 = ebase + nbase + (lane & 31), r1 = r0 + 32;
-    src.s0 = m.s + r0 * Kg; src.b0 = m.b + r0 * Kg;
-    src.s1 = m.s + r1 * Kg; src.b1 = m.b + r1 * Kg;
+    for (int q = 0; q < 4; ++q) src.q[q] = m.q + uniform_size((ebase + nbase + 16 * q) * Kq);
+    src.qrow = (uint32_t)(lane >> 2) * Kq;
+    src.c16 = 16u * ((lane & 3) ^ ((lane >> 4) & 3));
+    const size_t o0 = uniform_size((ebase + nbase) * Kg), o1 = o0 + 32 * Kg;
+    src.s0 = m.s + o0; src.b0 = m.b + o0;
+    src.s1 = m.s + o1; src.b1 = m.b + o1;
+    src.soff = (uint32_t)(lane & 31) * Kg * 2u;
     src.kbytes = Kq;
     src.ngroups = Kg;
     f32x16 acc0[MS], acc1[MS];
-    mainloop<MS, G>(rowp, K, src, L, acc0, acc1);
+    mainloop<MS, G>(hsrc, aoff, K, src, L, acc0, acc1);
     // epilogue: o = w_route * acc as bf16 into an LDS tile [MS*32 rows][256
     // cols] (512-byte rows; rows 32 q .. 32 q + 31 in the q-th of four LDS
     // objects), then 16-byte coalesced stores of 512-byte row segments
@@ -482,7 +511,7 @@ __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows,
     for (int it = 0; it < MS * 4; ++it) {
         const int m = (threadIdx.x >> 5) + 8 * it;
         if (m < rows && col < a.d) {
-            const uint8_t *rowb = part[m >> 5] + (m & 31) * 512;
+            const uint8_t *rowb = part[it >> 2] + (m & 31) * 512;  // m >> 5 == it >> 2
             *reinterpret_cast<uint4 *>(a.obuf + (size_t)(orow0 + m) * a.d + col) =
                 *reinterpret_cast<const uint4 *>(rowb + chunk * 16);
         }

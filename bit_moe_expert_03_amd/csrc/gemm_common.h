@@ -51,6 +51,20 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblk_pad)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// A 64-bit integer that is the same in every lane, moved to SGPRs.  The
+// builtin returns a signed int: each half is taken back as uint32_t before
+// widening, so that bit 31 of the low half never spreads into the high half.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// an offset that is the same in every lane, moved to SGPRs (applied to
+// offsets rather than pointers, which keeps the pointers' address space)
+__device__ __forceinline__ size_t uniform_size(size_t v) { return (size_t)uniform_u64((uint64_t)v); }
+
 // wait until at most N vector-memory operations of this wave are in flight
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -66,7 +80,9 @@ __device__ __forceinline__ void wait_vmcnt()
 __device__ __forceinline__ void block_sync()
 {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");       // no LDS access moves across the barrier
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // scale/bias words of one pair for the lane's two rows (NW words of two

@@ -73,7 +73,8 @@ typedef enum {
 
 /* Layer shape.  Supported: 0 <= T <= 2^22 (T*k < 2^31); 1 <= k <= E <= 256;
  * G in {32, 64, 128}; d, F and Fs positive multiples of 64 and of G, at most
- * 16384.  tile_m: height of a block-map tile, one of {32, 64, 128}, or 0 to
+ * 16384; T*d, T*k*F and T*Fs below 2^31 (each activation matrix of the
+ * prefill path under 4 GiB, addressed with 32-bit offsets).  tile_m: height of a block-map tile, one of {32, 64, 128}, or 0 to
  * let the library pick from T*k/E (moe_tile_m reports the choice). */
 typedef struct {
     int32_t T, d, E, k, F, Fs, G, tile_m;

@@ -57,6 +57,8 @@ def test_explicit_tile_m_is_kept():
 BAD = [
     dict(E=0), dict(E=257), dict(k=0), dict(k=17), dict(G=16), dict(d=96), dict(F=100),
     dict(Fs=0), dict(T=-1), dict(tile_m=48), dict(d=64 * 300),
+    # activation matrices of 2^31 elements or more (32-bit byte offsets)
+    dict(T=1 << 20, d=2048), dict(T=1 << 20, k=8, F=256), dict(T=1 << 20, Fs=2048),
 ]
 
 
