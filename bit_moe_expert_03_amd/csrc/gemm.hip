@@ -415,16 +415,17 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gateup_kernel(GateUpArgs 
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b2[kBBuf];
-    const int L = xcd_logical_block(blockIdx.x, a.nblk_pad);
+    const int nblk_r = max(0, min(*a.tiles.num_tiles, a.tiles.max_tiles)) * a.ntn_r;  // routed blocks with work
+    const int L = xcd_logical_block(blockIdx.x, nblk_r + a.nblk_s);
+    if (L < 0) return;
     int row0, rows, N, nt;
     const moe_qmat *mg, *mu;
     size_t ebase;  // first row of the expert's slab
     uint16_t *out;
     bool routed;
-    if (L < a.nblk_r) {
+    if (L < nblk_r) {
         const int tile = L / a.ntn_r;
         nt = L - tile * a.ntn_r;
-        if (tile >= *a.tiles.num_tiles) return;
         const int e = a.tiles.tile_expert[tile];
         row0 = a.tiles.tile_row0[tile];
         rows = a.tiles.tile_rows[tile];
@@ -432,17 +433,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gateup_kernel(GateUpArgs 
         ebase = (size_t)e * a.F;
         out = a.h_r;
         routed = true;
-    } else if (L < a.nblk_r + a.nblk_s) {
-        const int tile = (L - a.nblk_r) / a.ntn_s;
-        nt = (L - a.nblk_r) - tile * a.ntn_s;
+    } else {
+        const int tile = (L - nblk_r) / a.ntn_s;
+        nt = (L - nblk_r) - tile * a.ntn_s;
         row0 = tile * BM;
         rows = min(BM, a.T - row0);
         N = a.Fs; mg = &a.sgate; mu = &a.sup;
         ebase = 0;
         out = a.h_s;
         routed = false;
-    } else {
-        return;
     }
     const int msub = (rows + 31) >> 5;  // live 32-row sub-tiles (block-uniform)
     if (BM >= 128 && msub > 2)
@@ -526,34 +525,33 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b2[kBBuf];
-    const int L = xcd_logical_block(blockIdx.x, a.nblk_pad);
+    const int nblk_r = max(0, min(*a.tiles.num_tiles, a.tiles.max_tiles)) * a.ntn;  // routed blocks with work
+    const int L = xcd_logical_block(blockIdx.x, nblk_r + a.nblk_s);
+    if (L < 0) return;
     int row0, rows, K, nt;
     const moe_qmat *m;
     size_t ebase;
     const uint16_t *hsrc;
     int orow0;  // first output row in obuf
     bool routed;
-    if (L < a.nblk_r) {
+    if (L < nblk_r) {
         const int tile = L / a.ntn;
         nt = L - tile * a.ntn;
-        if (tile >= *a.tiles.num_tiles) return;
         ebase = (size_t)a.tiles.tile_expert[tile] * a.d;
         row0 = a.tiles.tile_row0[tile];
         rows = a.tiles.tile_rows[tile];
         K = a.F; m = &a.down; hsrc = a.h_r;
         orow0 = row0;
         routed = true;
-    } else if (L < a.nblk_r + a.nblk_s) {
-        const int tile = (L - a.nblk_r) / a.ntn;
-        nt = (L - a.nblk_r) - tile * a.ntn;
+    } else {
+        const int tile = (L - nblk_r) / a.ntn;
+        nt = (L - nblk_r) - tile * a.ntn;
         row0 = tile * BM;
         rows = min(BM, a.T - row0);
         ebase = 0;
         K = a.Fs; m = &a.sdown; hsrc = a.h_s;
         orow0 = a.T * a.k + row0;
         routed = false;
-    } else {
-        return;
     }
     const int msub = (rows + 31) >> 5;
     if (BM >= 128 && msub > 2)
@@ -616,9 +614,8 @@ static hipError_t launch_bm(const Plan &p, const uint16_t *x, const moe_weights 
     g.tiles = tiles;
     g.ntn_r = (p.F + 127) / 128;
     g.ntn_s = (p.Fs + 127) / 128;
-    g.nblk_r = (int)p.max_tiles * g.ntn_r;
     g.nblk_s = shared_tiles * g.ntn_s;
-    g.nblk_pad = (g.nblk_r + g.nblk_s + 7) & ~7;
+    g.nblk_pad = ((int)p.max_tiles * g.ntn_r + g.nblk_s + 7) & ~7;
     g.h_r = h_r; g.h_s = h_s;
     launch(tr, moe_gateup_kernel<BM, G>, dim3(g.nblk_pad), dim3(kGemmThreads), 0, s, g);
 
@@ -629,9 +626,8 @@ static hipError_t launch_bm(const Plan &p, const uint16_t *x, const moe_weights 
     dn.tiles = tiles;
     dn.ntn = (p.d + 255) / 256;
     dn.obuf = obuf;
-    dn.nblk_r = (int)p.max_tiles * dn.ntn;
     dn.nblk_s = shared_tiles * dn.ntn;
-    dn.nblk_pad = (dn.nblk_r + dn.nblk_s + 7) & ~7;
+    dn.nblk_pad = ((int)p.max_tiles * dn.ntn + dn.nblk_s + 7) & ~7;
     launch(tr, moe_down_kernel<BM, G>, dim3(dn.nblk_pad), dim3(kGemmThreads), 0, s, dn);
 
     launch(tr, moe_combine_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, (const uint16_t *)obuf,

@@ -22,8 +22,8 @@ struct GateUpArgs {
     moe_qmat gate, up, sgate, sup;
     GemmTiles tiles;
     int ntn_r, ntn_s;       // 128-column blocks per tile (routed, shared)
-    int nblk_r, nblk_s;     // blocks of the routed and the shared part
-    int nblk_pad;           // grid size (multiple of 8)
+    int nblk_s;             // blocks of the shared part (the routed part: num_tiles * ntn_r)
+    int nblk_pad;           // grid size: routed blocks of max_tiles tiles + nblk_s, multiple of 8
     uint16_t *h_r;          // [T*k][F] sorted rows
     uint16_t *h_s;          // [T][Fs]
 };
@@ -36,17 +36,23 @@ struct DownArgs {
     moe_qmat down, sdown;
     GemmTiles tiles;
     int ntn;                // 256-column blocks (d / 256, rounded up)
-    int nblk_r, nblk_s, nblk_pad;
+    int nblk_s, nblk_pad;   // as in GateUpArgs
     uint16_t *obuf;         // [T*k + T][d] weighted outputs: sorted routed rows, then shared
 };
 
-// Blocks are dispatched round-robin over the 8 XCDs; renumber them so that
-// consecutive logical blocks (the column blocks of one tile, then the next
-// tile of the same expert) run on the same XCD and share its L2.
-__device__ __forceinline__ int xcd_logical_block(int bid, int nblk_pad)
+// Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8).  The grid is sized for the largest possible tile count, while the
+// count of blocks with work is known only on the device.  Give each XCD an
+// equal contiguous range of the blocks that have work, so that consecutive
+// logical blocks (the column blocks of one tile, then the next tile of the
+// same expert) run on the same XCD and share its L2.  -1: no work.
+__device__ __forceinline__ int xcd_logical_block(int bid, int total)
 {
-    const int per = nblk_pad >> 3;
-    return (bid & 7) * per + (bid >> 3);
+    const int per = (total + 7) >> 3;
+    const int i = bid >> 3;
+    if (i >= per) return -1;
+    const int L = (bid & 7) * per + i;
+    return L < total ? L : -1;
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
