@@ -33,8 +33,10 @@
 // contraction index of slot j in sub-step s of a 64-wide K step is
 // k = 32 h + 8 s + j for BOTH operands (any common assignment is valid),
 // which makes each lane's B codes one contiguous 16-byte load and its A
-// operand one contiguous 16-byte LDS read.  Accumulator register r of lane l
-// is D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+// operand one contiguous 16-byte LDS read.  The weights are the first
+// operand, so the accumulators hold the transposed tile: register r of lane
+// l is D[row l % 32][column 8 (r / 4) + 4 (l / 32) + r % 4], one output row
+// per lane, which the epilogues store straight from registers.
 #include "gemm_common.h"
 
 namespace moe {
@@ -63,14 +65,17 @@ constexpr int kBBuf = 4 * kBWave;                 // 16 KB per buffer
 // Issued from inline assembly so that the compiler does not treat LDS reads
 // of the other buffers as dependent on it (it would wait for every copy in
 // flight before each of them); the main loop counts these copies itself
-// (wait_vmcnt) and fences them with the barrier.  The s_nop covers both the
+// (wait_vmcnt).  No memory clobber: a copy writes an LDS buffer that no wave
+// reads until after the next block_sync, whose compiler fences keep every
+// LDS access on its side of the barrier, so the LDS reads of the current
+// step may be scheduled freely around the copies.  The s_nop covers both the
 // M0 write and a base just moved into SGPRs by a VALU readfirstlane.
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint8_t *lds)
 {
     const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds);
     const uint64_t sb = uniform_u64((uint64_t)(uintptr_t)base);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(sb)
-                 : "memory", "m0");
+                 : "m0");
 }
 
 // Copy the A tile of K step kt (MS*32 rows x 64 bf16) into an A stage:
@@ -105,9 +110,14 @@ struct BSrc {
 // chunk c of row r lands in slot c ^ ((r >> 2) & 3) (src.c16 holds the chunk
 // of this lane's slot).  In the half pair at the end of an odd step count the
 // window is clamped to the row.
+__device__ __forceinline__ uint32_t b_offset(const BSrc &src, int p)
+{
+    return src.qrow + min(64u * p + src.c16, (uint32_t)src.kbytes - 16u);
+}
+
 __device__ __forceinline__ void b_dma(const BSrc &src, int p, uint8_t *wave_buf)
 {
-    const uint32_t off = src.qrow + min(64u * p + src.c16, (uint32_t)src.kbytes - 16u);
+    const uint32_t off = b_offset(src, p);
 #pragma unroll
     for (int q = 0; q < 4; ++q) dma16(src.q[q], off, wave_buf + q * 1024);
 }
@@ -190,16 +200,49 @@ __device__ __forceinline__ void decode_first(const StepCodes &sc, const StepScal
     f.o1 = decode_sub(sc.w1[0], t.s1, t.b1);
 }
 
+// Copies a K step issues for later steps: the A tile of the next step and,
+// at the first step of a pair (B), the codes of the pair two ahead.
+template <int MS, bool B>
+struct StepCopies {
+    const uint16_t *a_src;       // A base at the next step's K offset
+    const uint32_t (&aoff)[MS];  // this lane's A offsets
+    uint8_t *a_dst;              // next A stage
+    const BSrc &b;
+    uint32_t b_off;              // this lane's code offset in the pair two ahead
+    uint8_t *b_dst;              // that pair's buffer (this wave's slice)
+
+    // The copies of sub-step s: A in sub-steps 0 and 1, codes in 2 and 3, at
+    // most two per sub-step.  Issued all at once, the copies of a step (up to
+    // 64 KB per CU) queue behind each other and a wave whose copy cannot
+    // enter the full queue stalls with all its matrix-core work behind it.
+    // The codes stay the last copies of the step, which the entry wait of
+    // the next step relies on.
+    __device__ __forceinline__ void issue(int s) const
+    {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+        for (int i = 0; i < MS; ++i)
+            if ((2 * i) / MS == s) dma16(a_src, aoff[i], a_dst + (4 * i + wave) * 1024);
+        if constexpr (B) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (2 + q / 2 == s) dma16(b.q[q], b_off, b_dst + q * 1024);
+        }
+    }
+};
+
 // One 64-wide K step.  The codes of this step (cur) were read and its first
 // sub-step decoded (first) during the previous step; the four 16-wide MFMA
 // sub-steps are software pipelined (decode and A reads of sub-step s+1 under
 // the MFMAs of s), and under the MFMAs of the last sub-step the codes of the
 // next step are read from LDS (bnext, step jn of its pair) and its first
-// sub-step is decoded, so the next step starts with matrix-core work.
-template <int MS, int G>
+// sub-step is decoded, so the next step starts with matrix-core work.  The
+// copies for later steps are spread over the sub-steps (cp).
+template <int MS, int G, bool B>
 __device__ __forceinline__ void kstep(const uint8_t *astage, const StepCodes &cur, const StepScales &sc,
                                       const FirstOps &first, const uint8_t *bnext, SBPair<G> &sbnext, int jn,
-                                      StepCodes &nxt, FirstOps &nfirst, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
+                                      StepCodes &nxt, FirstOps &nfirst, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS],
+                                      const StepCopies<MS, B> &cp)
 {
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, n = lane & 31;
@@ -215,6 +258,7 @@ __device__ __forceinline__ void kstep(const uint8_t *astage, const StepCodes &cu
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int cu = s & 1, nx = cu ^ 1;
+        cp.issue(s);
         bf16x8 av[MS];
 #pragma unroll
         for (int i = 0; i < MS; ++i) av[i] = aread(i, s);
@@ -232,8 +276,8 @@ __device__ __forceinline__ void kstep(const uint8_t *astage, const StepCodes &cu
         }
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
-            acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], o0[cu], acc0[i], 0, 0, 0);
-            acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], o1[cu], acc1[i], 0, 0, 0);
+            acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0[cu], av[i], acc0[i], 0, 0, 0);
+            acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1[cu], av[i], acc1[i], 0, 0, 0);
         }
         interleave_hint<2 * MS, 0>();
     }
@@ -259,13 +303,13 @@ struct Carry {
 // One K step.  ST = kt % 6 fixes J = kt & 1 (A stage, step inside the pair)
 // and PB = (kt / 2) % 3 (B buffer of the pair).  Codes are copied two pairs
 // ahead, A one step ahead, scales one pair ahead (registers).  Issue order
-// at J = 0: the scale loads of pair p+1, the copies of A(kt+1), then those
-// of pair p+2 (into the buffer of pair p-1, last read one step before this
-// one); at J = 1 the copies of A(kt+1).  Entry wait: at J = 1 the scales and
-// this wave's copy of A(kt) must have landed, the 4 code copies issued after
-// them need not; at J = 0 everything, which includes the codes of pair p+1
-// that the end of the next step reads.  After the barrier every wave's
-// copies up to there are in LDS.
+// at J = 0: the scale loads of pair p+1, then (spread over the sub-steps) the
+// copies of A(kt+1) and those of pair p+2 (into the buffer of pair p-1, last
+// read one step before this one); at J = 1 the copies of A(kt+1).  Entry
+// wait: at J = 1 the scales and this wave's copy of A(kt) must have landed,
+// the 4 code copies issued after them need not; at J = 0 everything, which
+// includes the codes of pair p+1 that the end of the next step reads.  After
+// the barrier every wave's copies up to there are in LDS.
 template <int MS, int G, int ST>
 __device__ __forceinline__ void mainloop_step(int kt, int nk, int npair, const uint16_t *abase,
                                               const uint32_t (&aoff)[MS], const BSrc &bsrc, const LdsBufs &L,
@@ -275,15 +319,15 @@ __device__ __forceinline__ void mainloop_step(int kt, int nk, int npair, const u
     if constexpr (J == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
     block_sync();
     if constexpr (J == 0) sb_load<G>(cs.sbn, bsrc, min((kt >> 1) + 1, npair - 1));
-    a_dma<MS>(abase, aoff, min(kt + 1, nk - 1), L.a<J ^ 1>());
-    if constexpr (J == 0) b_dma(bsrc, min((kt >> 1) + 2, npair - 1), L.b<(PB + 2) % 3>());
+    const StepCopies<MS, J == 0> cp = {abase + min(kt + 1, nk - 1) * kKStep, aoff, L.a<J ^ 1>(), bsrc,
+                                       b_offset(bsrc, min((kt >> 1) + 2, npair - 1)), L.b<(PB + 2) % 3>()};
     // next step: same pair at J = 0, first step of the next pair at J = 1
     constexpr int PBN = J == 0 ? PB : (PB + 1) % 3;
     const StepCodes cur = cs.codes;
     const FirstOps first = cs.first;
     const StepScales sc = step_scales<G>(cs.sb, J);
-    kstep<MS, G>(L.a<J>(), cur, sc, first, L.b<PBN>(), J == 0 ? cs.sb : cs.sbn, J ^ 1, cs.codes, cs.first, acc0,
-                 acc1);
+    kstep<MS, G, J == 0>(L.a<J>(), cur, sc, first, L.b<PBN>(), J == 0 ? cs.sb : cs.sbn, J ^ 1, cs.codes, cs.first,
+                         acc0, acc1, cp);
     if constexpr (J == 1) cs.sb = cs.sbn;
 }
 
@@ -380,29 +424,15 @@ __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int r
     src.ngroups = Kg;
     f32x16 accg[MS], accu[MS];
     mainloop<MS, G>(a.x, aoff, a.d, src, L, accg, accu);
-    // epilogue: h = bf16(silu(g) * u) into an LDS tile [MS*32 rows][128 cols]
-    // (rows 0..63 in lds_b0, 64..127 in lds_b1, 256-byte rows), then 16-byte
-    // coalesced stores of whole 256-byte row segments
-    block_sync();  // every wave is done reading the last A stage and B buffer
-    const int half = lane >> 5;
-    const int n = lane & 31;
+    // epilogue: h = bf16(silu(g) * u), one row per lane, 16-byte stores
+    if (ncol0 < N) {
 #pragma unroll
-    for (int i = 0; i < MS; ++i)
+        for (int i = 0; i < MS; ++i) {
+            const int m = 32 * i + (lane & 31);
+            float v[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-            uint8_t *rowb = (m < 64 ? lds_b0 : lds_b1) + (m & 63) * 256;
-            *reinterpret_cast<uint16_t *>(rowb + (32 * wave + n) * 2) = f32_to_bf16(silu(accg[i][r]) * accu[i][r]);
-        }
-    block_sync();
-    const int chunk = threadIdx.x & 15, col = nt * 128 + chunk * 8;
-#pragma unroll
-    for (int it = 0; it < MS * 2; ++it) {
-        const int m = (threadIdx.x >> 4) + 16 * it;
-        if (m < rows && col < N) {
-            const uint8_t *rowb = (m < 64 ? lds_b0 : lds_b1) + (m & 63) * 256;
-            *reinterpret_cast<uint4 *>(out + (size_t)(row0 + m) * N + col) =
-                *reinterpret_cast<const uint4 *>(rowb + chunk * 16);
+            for (int r = 0; r < 16; ++r) v[r] = silu(accg[i][r]) * accu[i][r];
+            if (m < rows) store_row32(out + (size_t)(row0 + m) * N + ncol0, v);
         }
     }
 }
@@ -458,11 +488,13 @@ __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows,
                                           int orow0, bool routed, int nt, uint8_t *lds_a0,
                                           uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1, uint8_t *lds_b2)
 {
-    // routing weight of routed row tid of the tile; staged into LDS for the
-    // epilogue once the main loop has freed the third B buffer
-    float wrow = 1.0f;
-    if (routed && threadIdx.x < MS * 32) wrow = a.topk_w[a.perm[row0 + min((int)threadIdx.x, rows - 1)]];
     const int lane = threadIdx.x & 63;
+    // routing weight of this lane's output row in each sub-tile (the shared
+    // expert's rows have weight 1), loaded before the main loop
+    float wrow[MS];
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+        wrow[i] = routed ? a.topk_w[a.perm[row0 + min(32 * i + (lane & 31), rows - 1)]] : 1.0f;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wslice = wave * kBWave;
     const LdsBufs L = {lds_a0, lds_a1, lds_b0 + wslice, lds_b1 + wslice, lds_b2 + wslice};
@@ -484,35 +516,20 @@ __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows,
     src.ngroups = Kg;
     f32x16 acc0[MS], acc1[MS];
     mainloop<MS, G>(hsrc, aoff, K, src, L, acc0, acc1);
-    // epilogue: o = w_route * acc as bf16 into an LDS tile [MS*32 rows][256
-    // cols] (512-byte rows; rows 32 q .. 32 q + 31 in the q-th of four LDS
-    // objects), then 16-byte coalesced stores of 512-byte row segments
-    block_sync();
-    float *row_w = reinterpret_cast<float *>(lds_b2);
-    if (threadIdx.x < MS * 32) row_w[threadIdx.x] = wrow;
-    block_sync();
-    const int half = lane >> 5;
-    const int n = lane & 31;
-    uint8_t *const part[4] = {lds_b0, lds_b1, lds_a0, lds_a1};
+    // epilogue: o = w_route * acc as bf16, one row per lane, 16-byte stores
+    if (ncol0 < a.d) {
 #pragma unroll
-    for (int i = 0; i < MS; ++i)
+        for (int i = 0; i < MS; ++i) {
+            const int m = 32 * i + (lane & 31);
+            if (m >= rows) continue;
+            uint16_t *orow = a.obuf + (size_t)(orow0 + m) * a.d + ncol0;
+            float v[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-            const float wr = routed ? row_w[m] : 1.0f;
-            uint8_t *rowb = part[i] + (m & 31) * 512;
-            *reinterpret_cast<uint16_t *>(rowb + (64 * wave + n) * 2) = f32_to_bf16(wr * acc0[i][r]);
-            *reinterpret_cast<uint16_t *>(rowb + (64 * wave + n + 32) * 2) = f32_to_bf16(wr * acc1[i][r]);
-        }
-    block_sync();
-    const int chunk = threadIdx.x & 31, col = nt * 256 + chunk * 8;
+            for (int r = 0; r < 16; ++r) v[r] = wrow[i] * acc0[i][r];
+            store_row32(orow, v);
 #pragma unroll
-    for (int it = 0; it < MS * 4; ++it) {
-        const int m = (threadIdx.x >> 5) + 8 * it;
-        if (m < rows && col < a.d) {
-            const uint8_t *rowb = part[it >> 2] + (m & 31) * 512;  // m >> 5 == it >> 2
-            *reinterpret_cast<uint4 *>(a.obuf + (size_t)(orow0 + m) * a.d + col) =
-                *reinterpret_cast<const uint4 *>(rowb + chunk * 16);
+            for (int r = 0; r < 16; ++r) v[r] = wrow[i] * acc1[i][r];
+            store_row32(orow + 32, v);
         }
     }
 }

@@ -119,6 +119,36 @@ __device__ __forceinline__ bf16x8 decode_sub(uint32_t w, float s, float b)
     return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
+// Store 32 columns of one output row from an accumulator of the transposed
+// product (weights as the first MFMA operand): lane l holds row l % 32 of its
+// sub-tile, and registers 4 g .. 4 g + 3 hold columns 8 g + 4 h .. 8 g + 4 h
+// + 3, h = l / 32.  The values are packed to bf16, then the two halves of
+// the wave swap chunks (v_permlane32_swap: the upper half of the first
+// operand with the lower half of the second) so that each lane holds 16
+// contiguous bytes, columns 16 p + 8 h .. 16 p + 8 h + 7 for p = 0, 1.
+// rowp: column 0 of the lane's row (16-byte aligned).
+__device__ __forceinline__ void store_row32(uint16_t *rowp, const float (&v)[16])
+{
+    const int h = (threadIdx.x & 63) >> 5;
+    uint32_t d[4][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        d[g][0] = pack_bf16x2(v[4 * g], v[4 * g + 1]);
+        d[g][1] = pack_bf16x2(v[4 * g + 2], v[4 * g + 3]);
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto r = __builtin_amdgcn_permlane32_swap(d[2 * p][w], d[2 * p + 1][w], false, false);
+            d[2 * p][w] = r[0];
+            d[2 * p + 1][w] = r[1];
+        }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+        *reinterpret_cast<uint4 *>(rowp + 16 * p + 8 * h) = make_uint4(d[2 * p][0], d[2 * p][1], d[2 * p + 1][0], d[2 * p + 1][1]);
+}
+
 // scheduling hint: interleave n MFMAs with the decode VALU and LDS reads of
 // the next sub-step (6 VALU ops fit under one 32x32x16 MFMA)
 template <int NMFMA, int NDS>
