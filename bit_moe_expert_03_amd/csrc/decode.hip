@@ -53,6 +53,14 @@ struct DecodeArgs {
 
 // ---- packed 4-bit dot products ---------------------------------------------
 
+// a.lo * b.lo + a.hi * b.hi + c for bf16 pairs a, b (fp32 products and sum)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+constexpr uint32_t kBf16Ones = 0x3F803F80u;  // the bf16 pair (1.0, 1.0)
+
 // 32 elements of a bf16 vector as the bf16 pairs in the order dot_codes32()
 // pairs the codes, and their fp32 sum
 struct VecChunk {
@@ -70,15 +78,12 @@ __device__ __forceinline__ void vec_chunk(const uint4 (&w)[4], VecChunk &v)
         v.p[4 * g + 1] = __builtin_amdgcn_perm(w3, w2, 0x05040100u);  // (x4, x6)
         v.p[4 * g + 2] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);  // (x1, x3)
         v.p[4 * g + 3] = __builtin_amdgcn_perm(w3, w2, 0x07060302u);  // (x5, x7)
-        const uint32_t ws[4] = {w0, w1, w2, w3};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v.sum += bf16_to_f32(ws[i] & 0xFFFFu) + bf16_to_f32(ws[i] >> 16);
+        // the chunk sum as dot products with the bf16 pair (1, 1), fp32 accumulation
+        v.sum = dot2_bf16(w0, kBf16Ones, v.sum);
+        v.sum = dot2_bf16(w1, kBf16Ones, v.sum);
+        v.sum = dot2_bf16(w2, kBf16Ones, v.sum);
+        v.sum = dot2_bf16(w3, kBf16Ones, v.sum);
     }
-}
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
-{
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
 // sum over the chunk of (128 + q_i) * v_i for the 32 codes in q
