@@ -139,11 +139,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Top-k of one row of E <= 256 logits by one wave.  Lane l holds experts
-// 4l .. 4l+3, so among lanes holding the largest key the lowest lane holds
-// the lowest id.  Each round: wave max of the ordered keys (DPP), the lowest
-// lane and slot holding it (ballot, find-first), clear that slot.  Selected
-// (id, logit) of round j end up in lane j % 64, register j / 64.
+// Top-k of one row of E <= 256 logits by one wave (rounds of the selection
+// below).  Selected (id, logit) of round j end up in lane j % 64, register
+// j / 64.
 struct TopK {
     int id[4];
     float logit[4];
@@ -167,27 +165,53 @@ __device__ __forceinline__ LogitQuad load_logits(const float *__restrict__ L, in
     return q;
 }
 
-// One selection round over the wave's keys (lane l holds experts 4l .. 4l+3;
-// key 0 = no expert): the largest key m and its expert id (ties to the lower
-// id); the chosen key is cleared.
-__device__ __forceinline__ int topk_round(uint32_t (&key)[4], uint32_t &m)
+// The wave's keys for the selection rounds: lane l holds experts 4l .. 4l+3,
+// sorted once per lane by key descending, ties to the lower expert (key 0 =
+// no expert), so the lane's current largest key is k[0] and its expert slot
+// s[0].  A round is then one wave max of the lane heads, the lowest lane
+// holding it (ballot, find-first: lane order is expert order, so ties go to
+// the lower id), and a shift of that lane's list.
+struct LaneKeys {
+    uint32_t k[4];
+    int s[4];
+};
+
+__device__ __forceinline__ void lane_keys_cmpx(LaneKeys &t, int a, int b)
+{
+    const bool sw = t.k[a] < t.k[b] || (t.k[a] == t.k[b] && t.s[a] > t.s[b]);
+    const uint32_t ka = t.k[a], kb = t.k[b];
+    const int sa = t.s[a], sb = t.s[b];
+    t.k[a] = sw ? kb : ka; t.k[b] = sw ? ka : kb;
+    t.s[a] = sw ? sb : sa; t.s[b] = sw ? sa : sb;
+}
+
+__device__ __forceinline__ LaneKeys lane_keys(const uint32_t (&key)[4])
+{
+    LaneKeys t;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) { t.k[c] = key[c]; t.s[c] = c; }
+    // 4-input sorting network
+    lane_keys_cmpx(t, 0, 1); lane_keys_cmpx(t, 2, 3);
+    lane_keys_cmpx(t, 0, 2); lane_keys_cmpx(t, 1, 3);
+    lane_keys_cmpx(t, 1, 2);
+    return t;
+}
+
+// One selection round: the largest remaining key m and the lane holding it
+// (lowest lane on ties); that lane drops its head.  The expert is
+// 4 * lane + (its s[0] before the drop), read only when needed.
+__device__ __forceinline__ int topk_round(LaneKeys &t, uint32_t &m, int &slot)
 {
     const int lane = threadIdx.x & 63;
-    const uint32_t local = max(max(key[0], key[1]), max(key[2], key[3]));
-    m = wave_max_u32(local);
-    const uint64_t holders = __ballot(local == m);
-    const int wl = __ffsll((unsigned long long)holders) - 1;  // lowest lane with the max
-    int slot = 3;
-#pragma unroll
-    for (int c = 2; c >= 0; --c)
-        if (key[c] == m) slot = c;
-    slot = __builtin_amdgcn_readlane(slot, wl);
+    m = wave_max_u32(t.k[0]);
+    const uint64_t holders = __ballot(t.k[0] == m);
+    const int wl = __ffsll((unsigned long long)holders) - 1;
+    slot = t.s[0];
     if (lane == wl) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (c == slot) key[c] = 0u;
+        t.k[0] = t.k[1]; t.k[1] = t.k[2]; t.k[2] = t.k[3]; t.k[3] = 0u;
+        t.s[0] = t.s[1]; t.s[1] = t.s[2]; t.s[2] = t.s[3];
     }
-    return 4 * wl + slot;
+    return wl;
 }
 
 __device__ __forceinline__ void wave_topk(const LogitQuad &lq, int E, int k, TopK &out)
@@ -199,12 +223,15 @@ __device__ __forceinline__ void wave_topk(const LogitQuad &lq, int E, int k, Top
         const int e = 4 * lane + c;
         key[c] = (e < E) ? logit_key(lq.v[c]) : 0u;  // 0: no expert (finite keys are > 0)
     }
+    LaneKeys t = lane_keys(key);
 #pragma unroll
     for (int c = 0; c < 4; ++c) { out.id[c] = 0; out.logit[c] = 0.f; }
     out.lmax = 0.f;
     for (int j = 0; j < k; ++j) {
         uint32_t m;
-        const int id = topk_round(key, m);
+        int slot;
+        const int wl = topk_round(t, m, slot);
+        const int id = 4 * wl + __builtin_amdgcn_readlane(slot, wl);
         const float l = key_logit(m);
         if (j == 0) out.lmax = l;
 #pragma unroll
@@ -214,15 +241,15 @@ __device__ __forceinline__ void wave_topk(const LogitQuad &lq, int E, int k, Top
 }
 
 // Expert of rank j (0-based, ties to the lower id) among the wave's keys:
-// rounds 0 .. j of the selection above, nothing more (keys are consumed).
-__device__ __forceinline__ int wave_rank_expert(uint32_t (&key)[4], int j)
+// rounds 0 .. j of the selection above, nothing more.
+__device__ __forceinline__ int wave_rank_expert(const uint32_t (&key)[4], int j)
 {
-    int id = 0;
-    for (int r = 0; r <= j; ++r) {
-        uint32_t m;
-        id = topk_round(key, m);
-    }
-    return id;
+    LaneKeys t = lane_keys(key);
+    uint32_t m;
+    int slot;
+    for (int r = 0; r < j; ++r) topk_round(t, m, slot);
+    const int wl = topk_round(t, m, slot);
+    return 4 * wl + __builtin_amdgcn_readlane(slot, wl);
 }
 
 __device__ __forceinline__ float silu(float z)

@@ -159,6 +159,24 @@ def test_layer_full_size_sampled(name):
     check_y(c, g, ref, tokens=sample_tokens(c, ref))
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_tie_heavy_logits(seed):
+    """T = 1 with logits in {-1, -0, 0, 1}: most of the top 8 are exact ties.
+    Every routed wave of the decode kernel ranks the experts itself, so each
+    must break ties to the lower id as the oracle does (a wrong expert shows
+    in y as well as in the routing outputs of the fused path)."""
+    dims = wl.Dims(T=1, d=256, E=64, k=8, F=128, Fs=128, G=64)
+    c = wl.make_case(dims, seed=300 + seed)
+    rng = np.random.default_rng(seed)
+    L = rng.integers(-1, 2, (1, dims.E)).astype(np.float32)
+    L[0, rng.random(dims.E) < 0.3] = -0.0
+    c["logits"] = L
+    for mode in ("layer", "split"):
+        g = run(c, mode=mode)
+        ref = check_routing(c, g)
+        check_y(c, g, ref)
+
+
 @pytest.mark.parametrize("index", [0, 1])
 def test_decode_full_size(index):
     c = wl.make_case("c1_decode", index=index)
