@@ -60,7 +60,7 @@ def _declare(lib):
     lib.oracle_counting_sort.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _I32P, _I32P, _I32P, _I32P, _I32P]
     lib.oracle_block_map.argtypes = [ctypes.c_int, _I32P, _I32P, ctypes.c_int, ctypes.c_int, _I32P, _I32P, _I32P]
     lib.oracle_block_map.restype = ctypes.c_int
-    lib.oracle_ffn.argtypes = [ctypes.c_int] * 7 + [_U16P, ctypes.POINTER(_OWeights), _I32P, _F64P,
+    lib.oracle_ffn.argtypes = [ctypes.c_int] * 7 + [_U16P, ctypes.POINTER(_OWeights), _U16P, _I32P, _F64P,
                                                     _I32P, ctypes.c_int, ctypes.c_int, _F64P]
     return lib
 
@@ -156,8 +156,11 @@ def route(logits: np.ndarray, k: int, tile_m: int, max_tiles: Optional[int] = No
 
 
 def ffn(dims, x_bits: np.ndarray, weights: dict, ids: np.ndarray, w: np.ndarray,
-        tokens: Optional[Sequence[int]] = None, mirror: bool = False, lib=None) -> np.ndarray:
-    """y (fp64) for all tokens, or for the listed token indices: [len, d]."""
+        tokens: Optional[Sequence[int]] = None, mirror: bool = False, shared_gate=None,
+        lib=None) -> np.ndarray:
+    """y (fp64) for all tokens, or for the listed token indices: [len, d].
+    shared_gate: optional bf16 bits [d]; the shared expert's output is then
+    scaled by sigmoid(x_t . shared_gate) per token (else by 1)."""
     lib = lib or load()
     keep = []
 
@@ -178,6 +181,12 @@ def ffn(dims, x_bits: np.ndarray, weights: dict, ids: np.ndarray, w: np.ndarray,
         keep.append(tok)
         tok_p, ntok = _p(tok, _I32P), len(tok)
     y = np.empty((ntok, dims.d), np.float64)
+    sg_p = None
+    if shared_gate is not None:
+        sg = np.ascontiguousarray(shared_gate, dtype=np.uint16)
+        assert sg.shape == (dims.d,)
+        keep.append(sg)
+        sg_p = _p(sg, _U16P)
     lib.oracle_ffn(dims.T, dims.d, dims.E, dims.k, dims.F, dims.Fs, dims.G, _p(x_bits, _U16P),
-                   ctypes.byref(W), _p(ids, _I32P), _p(w, _F64P), tok_p, ntok, int(mirror), _p(y, _F64P))
+                   ctypes.byref(W), sg_p, _p(ids, _I32P), _p(w, _F64P), tok_p, ntok, int(mirror), _p(y, _F64P))
     return y

@@ -24,7 +24,10 @@
  * Readings of what the pages leave open (each is pinned by a CPU test):
  *  - top-k order: larger logit first, ties to the lower expert id, -0 == +0;
  *  - routing weights: softmax over the k selected logits (they sum to 1);
- *  - shared expert: weight 1, no gate, same 4-bit format as routed experts;
+ *  - shared expert: same 4-bit format as routed experts, weight 1; or, when
+ *    a gate vector g (bf16 [d]) is given, weight sigmoid(x . g) per token
+ *    (the pages name the always-on shared expert and nothing more; the
+ *    gated form is the optional variant of the library);
  *  - the scatter is stable: inside one expert, assignments a = t*k + j keep
  *    ascending order;
  *  - block map: for each expert in id order, tiles of tile_m consecutive
@@ -228,10 +231,21 @@ static omat expert_slab(const omat *m, int e, int rows, int cols, int G)
     return r;
 }
 
+/* Weight of the shared expert for token x: 1 without a gate vector, else
+ * the logistic sigmoid of the dot product x . g (fp64). */
+static double shared_weight(const double *x, const uint16_t *g, int d)
+{
+    if (!g) return 1.0;
+    double z = 0.0;
+    for (int i = 0; i < d; ++i) z += x[i] * bf16_value(g[i]);
+    return 1.0 / (1.0 + exp(-z));
+}
+
 /* y[ti][:] for the tokens tokens[0..ntok) (all T tokens if tokens == NULL):
- * y = sum_j w[t][j] * FFN_{ids[t][j]}(x_t) + FFN_shared(x_t), in fp64. */
+ * y = sum_j w[t][j] * FFN_{ids[t][j]}(x_t) + gamma_t * FFN_shared(x_t), in
+ * fp64, gamma_t = shared_weight(x_t, shared_gate). */
 void oracle_ffn(int T, int d, int E, int k, int F, int Fs, int G, const uint16_t *x,
-                const oweights *W, const int32_t *ids, const double *w,
+                const oweights *W, const uint16_t *shared_gate, const int32_t *ids, const double *w,
                 const int32_t *tokens, int ntok, int mirror, double *y)
 {
     (void)E;
@@ -255,7 +269,8 @@ void oracle_ffn(int T, int d, int E, int k, int F, int Fs, int G, const uint16_t
             for (int i = 0; i < d; ++i) yt[i] += w[(size_t)t * k + j] * o[i];
         }
         expert_ffn(&W->sgate, &W->sup, &W->sdown, d, Fs, G, xt, h, o, mirror);
-        for (int i = 0; i < d; ++i) yt[i] += o[i];
+        const double gamma = shared_weight(xt, shared_gate, d);
+        for (int i = 0; i < d; ++i) yt[i] += gamma * o[i];
         free(xt);
         free(h);
         free(o);

@@ -40,8 +40,10 @@ def swiglu_mlp(X, Wg, Wu, Wd):
     return h @ Wd.T
 
 
-def brute_layer(dims, x_bits, W, logits):
-    """y [T, d] fp64 = shared(x) + sum over ALL experts of mask[t,e] * FFN_e(x)."""
+def brute_layer(dims, x_bits, W, logits, shared_gate=None):
+    """y [T, d] fp64 = gamma * shared(x) + sum over ALL experts of
+    mask[t,e] * FFN_e(x); gamma = 1, or expit(x . g) per token with a gate
+    vector g (bf16 bits [d])."""
     T, E, k, G = dims.T, dims.E, dims.k, dims.G
     X = bf16_to_f64(x_bits)
     ids = topk_argsort(logits, k)
@@ -55,6 +57,8 @@ def brute_layer(dims, x_bits, W, logits):
     y = swiglu_mlp(X, unpack_dense(W["sgate"]["q"], W["sgate"]["s"], W["sgate"]["b"], G),
                    unpack_dense(W["sup"]["q"], W["sup"]["s"], W["sup"]["b"], G),
                    unpack_dense(W["sdown"]["q"], W["sdown"]["s"], W["sdown"]["b"], G))
+    if shared_gate is not None:
+        y = y * scipy.special.expit(X @ bf16_to_f64(shared_gate))[:, None]
     for e in range(E):
         y = y + mask[:, e:e + 1] * swiglu_mlp(X, Wg[e], Wu[e], Wd[e])
     return y, ids, wts

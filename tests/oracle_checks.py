@@ -287,9 +287,39 @@ def check_ffn_metamorphic(lib):
     np.testing.assert_array_equal(y3, y)
 
 
+def check_ffn_shared_gate(lib):
+    """Shared-expert gate: brute force (numpy dot, scipy expit) on small
+    shapes, and the limits of one token with g = +-64 x_0: the gate reads 1
+    (y equals the ungated layer exactly) and 0 (routed experts only); with
+    g = 0 it reads 1/2, halfway between the two."""
+    for i, dims in enumerate(SMALL_SHAPES):
+        c = wl.make_case(dims, seed=40 + i)
+        rng = np.random.default_rng(50 + i)
+        g = wl.to_bf16_bits((rng.standard_normal(dims.d) / np.sqrt(dims.d)).astype(np.float32))
+        r = oracle.route(c["logits"], dims.k, 16, lib=lib)
+        y = oracle.ffn(dims, c["x"], c["w"], r["ids"], r["w"], shared_gate=g, lib=lib)
+        yb, _, _ = brute_layer(dims, c["x"], c["w"], c["logits"], shared_gate=g)
+        err = np.abs(y - yb).max() / np.abs(yb).max()
+        assert err <= 1e-12, (dims, err)
+    dims = SMALL_SHAPES[0]
+    c = wl.make_case(dims, seed=45)
+    r = oracle.route(c["logits"], dims.k, 16, lib=lib)
+    x0 = bf16_to_f64(c["x"][0])
+    y_free = oracle.ffn(dims, c["x"], c["w"], r["ids"], r["w"], tokens=[0], lib=lib)
+    y_one = oracle.ffn(dims, c["x"], c["w"], r["ids"], r["w"], tokens=[0], lib=lib,
+                       shared_gate=torch_bf16_bits(64.0 * x0))
+    y_zero = oracle.ffn(dims, c["x"], c["w"], r["ids"], r["w"], tokens=[0], lib=lib,
+                        shared_gate=torch_bf16_bits(-64.0 * x0))
+    y_half = oracle.ffn(dims, c["x"], c["w"], r["ids"], r["w"], tokens=[0], lib=lib,
+                        shared_gate=np.zeros(dims.d, np.uint16))
+    np.testing.assert_array_equal(y_one, y_free)
+    assert np.abs(y_one - y_zero).max() > 1e-3 * np.abs(y_one).max()  # the shared part is not negligible
+    np.testing.assert_allclose(y_half, 0.5 * (y_one + y_zero), rtol=1e-12, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_packing_fixture, check_rounding_fixture, check_dequant_closed_form,
     check_dequant_general_rounding, check_route_fixture, check_topk_vs_argsort,
     check_weights_special, check_counting_sort, check_block_map, check_ffn_bruteforce,
-    check_ffn_single_expert_torch, check_ffn_integer, check_ffn_metamorphic,
+    check_ffn_single_expert_torch, check_ffn_integer, check_ffn_metamorphic, check_ffn_shared_gate,
 ]

@@ -25,7 +25,10 @@ MUTATIONS = [
     ("tile_rows_full", "(counts[e] - r0 < tile_m) ? counts[e] - r0 : tile_m", "tile_m"),
     ("silu_sign", "z / (1.0 + exp(-z))", "z / (1.0 + exp(z))"),
     ("gate_up_swapped", "h[n] = silu(g) * u;", "h[n] = silu(u) * g;"),
-    ("shared_dropped", "for (int i = 0; i < d; ++i) yt[i] += o[i];", "for (int i = 0; i < d; ++i) yt[i] += 0.0 * o[i];"),
+    ("shared_dropped", "yt[i] += gamma * o[i];", "yt[i] += 0.0 * gamma * o[i];"),
+    ("shared_gate_sign", "return 1.0 / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(z));"),
+    ("shared_gate_ignored", "const double gamma = shared_weight(xt, shared_gate, d);",
+     "const double gamma = shared_weight(xt, NULL, d);"),
     ("routing_weight_dropped", "yt[i] += w[(size_t)t * k + j] * o[i];", "yt[i] += o[i];"),
     ("down_transposed", "weight_at(down, Fw, G, i, n)", "weight_at(down, Fw, G, n % d, i % Fw)"),
     ("x_index", "xt[i] = bf16_value(x[(size_t)t * d + i]);", "xt[i] = bf16_value(x[(size_t)t + i]);"),
