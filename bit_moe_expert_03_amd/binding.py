@@ -38,7 +38,7 @@ class moe_qmat(ctypes.Structure):
 
 
 class moe_weights(ctypes.Structure):
-    _fields_ = [(n, moe_qmat) for n in MATS]
+    _fields_ = [(n, moe_qmat) for n in MATS] + [("shared_gate", ctypes.c_void_p)]
 
 
 ROUTING_FIELDS = ("topk_ids", "topk_w", "counts", "offsets", "perm", "inv_perm",
@@ -126,8 +126,11 @@ def moe_workspace_bytes(dims: moe_dims) -> int:
 
 
 def weights_struct(w: Dict[str, Dict[str, torch.Tensor]]) -> moe_weights:
-    """moe_weights from {'gate': {'q','s','b'}, ...} device tensors."""
-    return moe_weights(*[moe_qmat(_ptr(w[m]["q"]), _ptr(w[m]["s"]), _ptr(w[m]["b"])) for m in MATS])
+    """moe_weights from {'gate': {'q','s','b'}, ...} device tensors, plus an
+    optional 'shared_gate' entry (bf16 bits [d]) for the gated shared expert."""
+    sg = w.get("shared_gate")
+    return moe_weights(*[moe_qmat(_ptr(w[m]["q"]), _ptr(w[m]["s"]), _ptr(w[m]["b"])) for m in MATS],
+                       _ptr(sg) if sg is not None else None)
 
 
 def routing_struct(r: Dict[str, torch.Tensor]) -> moe_routing:

@@ -76,6 +76,7 @@ moe_status make_plan(const moe_dims *dm, Plan *p, const char **why)
     p->off_hs = off;   off = align_up(off + (size_t)d.T * d.Fs * 2);
     p->off_obuf = off; off = align_up(off + (size_t)(p->A + d.T) * d.d * 2);
     p->off_dech = off; off = align_up(off + (size_t)(d.k + 1) * Fmax * 4);
+    p->off_gamma = off; off = align_up(off + 4);  // decode: the shared expert's gate value
     p->ws_bytes = off;
     return MOE_OK;
 }
@@ -110,6 +111,8 @@ static moe_status check_weights(const Plan &p, const moe_weights *w)
     if ((st = check_qmat(w->up, "up", (int64_t)p.E * p.F, p.d, p.G))) return st;
     if ((st = check_qmat(w->down, "down", (int64_t)p.E * p.d, p.F, p.G))) return st;
     if ((st = check_qmat(w->sgate, "sgate", p.Fs, p.d, p.G))) return st;
+    if (w->shared_gate && (reinterpret_cast<uintptr_t>(w->shared_gate) & 15u))
+        return fail(MOE_ERR_ARG, "shared_gate: misaligned pointer");
     if ((st = check_qmat(w->sup, "sup", p.Fs, p.d, p.G))) return st;
     if ((st = check_qmat(w->sdown, "sdown", p.d, p.Fs, p.G))) return st;
     return MOE_OK;

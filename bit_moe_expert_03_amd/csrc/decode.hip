@@ -8,7 +8,8 @@
 //
 // Two kernels per layer:
 //   decode_gateup_kernel  block 0: top-k + softmax of the token's logits and
-//                         the routing outputs.  Every other wave owns
+//                         the routing outputs, and the shared expert's gate
+//                         value when it is gated.  Every other wave owns
 //                         P (gate, up) row pairs of one expert slot
 //                         and writes h_j[n] = bf16(silu(W_gate,j[n] . x) *
 //                         (W_up,j[n] . x)).  A wave of routed slot j needs
@@ -18,7 +19,7 @@
 //                         shared expert's waves load at once.  Slots are
 //                         ordered k-1 .. 0, shared last, so the waves with
 //                         the longest top-k are dispatched first.
-//   decode_down_kernel    y[i] = sum_j w_j (W_down,j[i] . h_j) + W_sdown[i] . h_s,
+//   decode_down_kernel    y[i] = sum_j w_j (W_down,j[i] . h_j) + gamma W_sdown[i] . h_s,
 //                         kDownRows output rows per block; lane = one
 //                         32-element chunk of the concatenated hidden vector
 //                         (shared expert first, its loads need no routing).
@@ -48,16 +49,11 @@ struct DecodeArgs {
     int d, E, k, F, Fs, G, Fmax;
     int wps_r, wps_s;     // work waves per routed slot, for the shared expert
     uint16_t *h;          // [k+1][Fmax] bf16 workspace: slots 0..k-1 routed, k shared
+    float *gamma;         // workspace: weight of the shared expert (gated variant)
     uint16_t *y;          // [1][d]
 };
 
 // ---- packed 4-bit dot products ---------------------------------------------
-
-// a.lo * b.lo + a.hi * b.hi + c for bf16 pairs a, b (fp32 products and sum)
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
-{
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
 
 constexpr uint32_t kBf16Ones = 0x3F803F80u;  // the bf16 pair (1.0, 1.0)
 
@@ -166,6 +162,30 @@ __device__ void decode_routing_block(const DecodeArgs &a)
     decode_write_routing(a, s_ids, s_w);
 }
 
+// block 0 of the gate/up grid, gated shared expert: gamma = sigmoid(x . g)
+__device__ void decode_shared_gate(const DecodeArgs &a)
+{
+    __shared__ float part[kDecThreads / kWave];
+    const int tid = threadIdx.x;
+    float z = 0.f;
+    for (int c = tid * 8; c < a.d; c += kDecThreads * 8) {
+        const uint4 xv = *reinterpret_cast<const uint4 *>(a.x + c);
+        const uint4 gv = *reinterpret_cast<const uint4 *>(a.w.shared_gate + c);
+        z = dot2_bf16(xv.x, gv.x, z);
+        z = dot2_bf16(xv.y, gv.y, z);
+        z = dot2_bf16(xv.z, gv.z, z);
+        z = dot2_bf16(xv.w, gv.w, z);
+    }
+    z = wave_sum(z);
+    if ((tid & 63) == 0) part[tid >> 6] = z;
+    __syncthreads();
+    if (tid == 0) {
+        float t = 0.f;
+        for (int w = 0; w < kDecThreads / kWave; ++w) t += part[w];
+        *a.gamma = 1.0f / (1.0f + __expf(-t));
+    }
+}
+
 // ---- gate/up -------------------------------------------------------------------
 
 // raw operands of one row for one 32-element chunk
@@ -188,6 +208,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
 {
     if (blockIdx.x == 0) {
         if (a.logits) decode_routing_block(a);
+        if (a.w.shared_gate) decode_shared_gate(a);
         return;
     }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -292,7 +313,7 @@ __global__ __launch_bounds__(kDownMaxThreads) void decode_down_kernel(DecodeArgs
         if (c < cFs) {  // shared expert: no routing needed
             j = a.k; f0 = c * 32; Fw = a.Fs; m = &a.w.sdown;
             ebase = 0;
-            wj = 1.0f;
+            wj = a.w.shared_gate ? *a.gamma : 1.0f;
         } else {
             j = (c - cFs) / cF; f0 = (c - cFs - j * cF) * 32; Fw = a.F; m = &a.w.down;
             ebase = (size_t)a.r.topk_ids[j] * a.d;
@@ -353,6 +374,7 @@ hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
     a.d = p.d; a.E = p.E; a.k = p.k; a.F = p.F; a.Fs = p.Fs; a.G = p.G;
     a.Fmax = p.F > p.Fs ? p.F : p.Fs;
     a.h = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + p.off_dech);
+    a.gamma = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_gamma);
     a.y = y;
     // F and Fs are multiples of 64, so every P below divides both
     const int nch = (p.d / 32 + kWave - 1) / kWave;

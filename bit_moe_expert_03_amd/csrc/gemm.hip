@@ -24,9 +24,10 @@
 //   moe_down_kernel     routed and shared tiles in one grid:
 //                       o = w_route * (h W_down^T) -> bf16 rows: routed rows
 //                       in sorted order, then the T shared rows (weight 1)
-//   moe_combine_kernel  y[t] = bf16(sum_j o[inv_perm[t k + j]] + o[T k + t]),
+//   moe_combine_kernel  y[t] = bf16(sum_j o[inv_perm[t k + j]] + gamma_t o[T k + t]),
 //                       slot order then shared, fp32: deterministic, no
-//                       atomics.
+//                       atomics; gamma_t = sigmoid(x_t . shared_gate) when
+//                       the shared expert is gated, else 1.
 //
 // MFMA 32x32x16 operand layout used (wave64): lane l holds row (A) or
 // column (B) l % 32 and the 8 contraction slots of half h = l / 32; the
@@ -583,24 +584,40 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
 __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__restrict__ obuf,
                                                           const int32_t *__restrict__ inv_perm,
                                                           int T, int k, int d,
+                                                          const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ shared_gate,
                                                           uint16_t *__restrict__ y)
 {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (t >= T) return;
     const int64_t shared_row = (int64_t)T * k + t;
+    float gamma = 1.0f;  // weight of the shared expert's row
+    if (shared_gate) {
+        float z = 0.f;
+        for (int c = lane * 8; c < d; c += 64 * 8) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(x + (int64_t)t * d + c);
+            const uint4 gv = *reinterpret_cast<const uint4 *>(shared_gate + c);
+            z = dot2_bf16(xv.x, gv.x, z);
+            z = dot2_bf16(xv.y, gv.y, z);
+            z = dot2_bf16(xv.z, gv.z, z);
+            z = dot2_bf16(xv.w, gv.w, z);
+        }
+        gamma = 1.0f / (1.0f + __expf(-wave_sum(z)));
+    }
     for (int c = lane * 8; c < d; c += 64 * 8) {
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
         for (int j = 0; j <= k; ++j) {
             const int64_t row = (j < k) ? (int64_t)inv_perm[(int64_t)t * k + j] : shared_row;
+            const float wr = (j < k) ? 1.0f : gamma;
             const uint4 v = *reinterpret_cast<const uint4 *>(obuf + row * d + c);
             const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[2 * i] += bf16_to_f32(wd[i] & 0xFFFFu);
-                acc[2 * i + 1] += bf16_to_f32(wd[i] >> 16);
+                acc[2 * i] += wr * bf16_to_f32(wd[i] & 0xFFFFu);
+                acc[2 * i + 1] += wr * bf16_to_f32(wd[i] >> 16);
             }
         }
         uint4 o;
@@ -648,7 +665,7 @@ static hipError_t launch_bm(const Plan &p, const uint16_t *x, const moe_weights 
     launch(tr, moe_down_kernel<BM, G>, dim3(dn.nblk_pad), dim3(kGemmThreads), 0, s, dn);
 
     launch(tr, moe_combine_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, (const uint16_t *)obuf,
-           (const int32_t *)r.inv_perm, p.T, p.k, p.d, y);
+           (const int32_t *)r.inv_perm, p.T, p.k, p.d, x, w.shared_gate, y);
     return hipGetLastError();
 }
 

@@ -93,6 +93,12 @@ __device__ __forceinline__ float dpp_f32(float v)
 
 // sum over the 64 lanes, broadcast to all: butterflies inside rows of 16
 // (quad permutes, row rotates), then row broadcasts 15 and 31 into lane 63
+// a.lo * b.lo + a.hi * b.hi + c for bf16 pairs a, b (fp32 products and sum)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
     v += dpp_f32<0xB1>(v);         // quad_perm [1,0,3,2]

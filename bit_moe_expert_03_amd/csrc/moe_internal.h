@@ -23,7 +23,7 @@ struct Plan {
     int route_nbp;      // route blocks rounded up to a multiple of 16 (histogram row pitch)
     int64_t max_tiles;  // length of the tile arrays
     // workspace carving (byte offsets)
-    size_t off_hist, off_hr, off_hs, off_obuf, off_dech, ws_bytes;
+    size_t off_hist, off_hr, off_hs, off_obuf, off_dech, off_gamma, ws_bytes;
 };
 
 // Optional per-kernel timing (measurement entry point): kernel i of a call

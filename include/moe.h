@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define MOE_API __attribute__((visibility("default")))
@@ -90,6 +90,12 @@ typedef struct {
 typedef struct {
     moe_qmat gate, up, down;    /* routed: [E][F][d], [E][F][d], [E][d][F] */
     moe_qmat sgate, sup, sdown; /* shared: [Fs][d], [Fs][d], [d][Fs] */
+    /* Optional gate of the shared expert, bf16 [d], 16-byte aligned, or NULL
+     * (weight 1).  With it the shared expert's output for token t is scaled
+     * by sigmoid(x_t . shared_gate), the dot product accumulated in fp32.
+     * The pages name an always-on shared expert and nothing more; the gated
+     * form is an optional variant (ABI version 2). */
+    const uint16_t *shared_gate;
 } moe_weights;
 
 /* Routing results (outputs of moe_route, inputs of moe_ffn).  Assignment

@@ -33,6 +33,8 @@ def run(case, tile_m=0, mode="layer", wdev=None, poison=True):
     dims = case["dims"]
     dm = B.make_dims(dims, tile_m)
     wdev = wdev if wdev is not None else weights_to_dev(case["w"])
+    if case.get("shared_gate") is not None:
+        wdev = dict(wdev, shared_gate=dev(case["shared_gate"]))
     logits = dev(case["logits"])
     x = dev(case["x"])
     r = B.alloc_routing(dm)
@@ -84,7 +86,8 @@ def y_tolerance(y_ref: np.ndarray) -> float:
 def check_y(case, g, ref_route, tokens=None):
     """y against the oracle on all tokens, or on the listed ones."""
     dims = case["dims"]
-    y_ref = oracle.ffn(dims, case["x"], case["w"], ref_route["ids"], ref_route["w"], tokens=tokens)
+    y_ref = oracle.ffn(dims, case["x"], case["w"], ref_route["ids"], ref_route["w"], tokens=tokens,
+                       shared_gate=case.get("shared_gate"))
     y = g["y"] if tokens is None else g["y"][np.asarray(tokens)]
     assert np.all(np.isfinite(g["y"])), "unwritten or non-finite outputs"
     err = float(np.abs(y - y_ref).max())

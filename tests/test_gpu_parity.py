@@ -159,6 +159,42 @@ def test_layer_full_size_sampled(name):
     check_y(c, g, ref, tokens=sample_tokens(c, ref))
 
 
+GATED = ["ragged_T37_E16_k4", "T300_E16_k4_G64", "T70_E8_k3_G128", "T1_small_decode", "zipf_T500_E64_k6"]
+
+
+@pytest.mark.parametrize("name", GATED)
+def test_layer_gated_shared_expert(name):
+    """Shared expert scaled by sigmoid(x . g) per token: both paths (GEMM
+    combine, decode down kernel), fused and split calls, two tile heights."""
+    c = dict(_case(name))
+    d = c["dims"].d
+    rng = np.random.default_rng(7)
+    c["shared_gate"] = wl.to_bf16_bits((rng.standard_normal(d) / np.sqrt(d)).astype(np.float32))
+    for mode, tile_m in (("layer", 0), ("split", 128)):
+        g = run(c, mode=mode, tile_m=tile_m)
+        ref = check_routing(c, g)
+        check_y(c, g, ref)
+
+
+def test_decode_gated_shared_expert_full_size():
+    c = dict(wl.make_case("c1_decode", index=3))
+    rng = np.random.default_rng(8)
+    c["shared_gate"] = wl.to_bf16_bits((rng.standard_normal(c["dims"].d) / np.sqrt(c["dims"].d)).astype(np.float32))
+    for mode in ("layer", "split"):
+        g = run(c, mode=mode)
+        ref = check_routing(c, g)
+        check_y(c, g, ref)
+
+
+def test_prefill_gated_shared_expert_sampled():
+    c = dict(wl.make_case("c2_prefill512"))
+    rng = np.random.default_rng(9)
+    c["shared_gate"] = wl.to_bf16_bits((rng.standard_normal(c["dims"].d) / np.sqrt(c["dims"].d)).astype(np.float32))
+    g = run(c)
+    ref = check_routing(c, g)
+    check_y(c, g, ref, tokens=sample_tokens(c, ref, n_random=32))
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_decode_tie_heavy_logits(seed):
     """T = 1 with logits in {-1, -0, 0, 1}: most of the top 8 are exact ties.
