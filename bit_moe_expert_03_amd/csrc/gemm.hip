@@ -256,13 +256,18 @@ __device__ __forceinline__ void kstep(const uint8_t *astage, const StepCodes &cu
     bf16x8 o0[2], o1[2];
     o0[0] = first.o0;
     o1[0] = first.o1;
+    // A operands one sub-step ahead: each register is reloaded for sub-step
+    // s+1 right after the two MFMAs of sub-step s that read it, so the LDS
+    // latency hides under the MFMAs of the other sub-tiles and no register
+    // is added (only the first sub-step's reads follow the barrier directly)
+    bf16x8 av[MS];
+#pragma unroll
+    for (int i = 0; i < MS; ++i) av[i] = aread(i, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // these reads first, all in flight together
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int cu = s & 1, nx = cu ^ 1;
         cp.issue(s);
-        bf16x8 av[MS];
-#pragma unroll
-        for (int i = 0; i < MS; ++i) av[i] = aread(i, s);
         if (s < 3) {
             o0[nx] = decode_sub(cur.w0[s + 1], sc.s0, sc.b0);
             o1[nx] = decode_sub(cur.w1[s + 1], sc.s1, sc.b1);
@@ -279,8 +284,9 @@ __device__ __forceinline__ void kstep(const uint8_t *astage, const StepCodes &cu
         for (int i = 0; i < MS; ++i) {
             acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0[cu], av[i], acc0[i], 0, 0, 0);
             acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1[cu], av[i], acc1[i], 0, 0, 0);
+            if (s < 3) av[i] = aread(i, s + 1);
         }
-        interleave_hint<2 * MS, 0>();
+        if (s < 3) interleave_pairs<MS, 1>(); else interleave_pairs<MS, 0>();
     }
 }
 

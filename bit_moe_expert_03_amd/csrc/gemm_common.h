@@ -162,4 +162,18 @@ __device__ __forceinline__ void interleave_hint()
     }
 }
 
+// scheduling hint for a sub-step of MS pairs of MFMAs: each pair (the two
+// MFMAs that read one A operand) is followed by NDS LDS reads (the operand's
+// reload for the next sub-step) and 12 VALU ops (decode of the next sub-step)
+template <int MS, int NDS>
+__device__ __forceinline__ void interleave_pairs()
+{
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+        if (NDS) __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // 12 VALU
+    }
+}
+
 }  // namespace moe

@@ -55,18 +55,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 // of byte m) of one affine group to 4 packed bf16 pairs, element 2r in the
 // low half of out[r].  Value = bf16_rne(fma(s, q, b)); s*q is exact in fp32,
 // so the fma rounds the exact s*q + b once.
+// Unpacking: a byte holding one code q (0..15) read as an OCP fp8 e4m3
+// value is q * 2^-9 exactly (codes 0..7 are the denormals m * 2^-9, codes
+// 8..15 the first normal binade (8 + m) * 2^-9), so one v_cvt_pk_f32_fp8
+// turns two isolated codes into fp32, and fma(512 s, q 2^-9, b) equals
+// fma(s, q, b) bit for bit (scaling by powers of two is exact for any scale
+// below 2^119).
+constexpr float kFp8CodeScale = 512.0f;
+
 __device__ __forceinline__ void dequant8_bf16(uint32_t v, float s, float b, uint32_t out[4])
 {
+    const float s9 = s * kFp8CodeScale;
     const uint32_t lo = v & 0x0F0F0F0Fu;         // elements 0,2,4,6
     const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;  // elements 1,3,5,7
-    out[0] = pack_bf16x2(__builtin_fmaf(s, ubyte_f32<0>(lo), b),
-                         __builtin_fmaf(s, ubyte_f32<0>(hi), b));
-    out[1] = pack_bf16x2(__builtin_fmaf(s, ubyte_f32<1>(lo), b),
-                         __builtin_fmaf(s, ubyte_f32<1>(hi), b));
-    out[2] = pack_bf16x2(__builtin_fmaf(s, ubyte_f32<2>(lo), b),
-                         __builtin_fmaf(s, ubyte_f32<2>(hi), b));
-    out[3] = pack_bf16x2(__builtin_fmaf(s, ubyte_f32<3>(lo), b),
-                         __builtin_fmaf(s, ubyte_f32<3>(hi), b));
+    const auto l01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);  // elements 0, 2
+    const auto l23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);   // elements 4, 6
+    const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);  // elements 1, 3
+    const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);   // elements 5, 7
+    out[0] = pack_bf16x2(__builtin_fmaf(s9, l01[0], b), __builtin_fmaf(s9, h01[0], b));
+    out[1] = pack_bf16x2(__builtin_fmaf(s9, l01[1], b), __builtin_fmaf(s9, h01[1], b));
+    out[2] = pack_bf16x2(__builtin_fmaf(s9, l23[0], b), __builtin_fmaf(s9, h23[0], b));
+    out[3] = pack_bf16x2(__builtin_fmaf(s9, l23[1], b), __builtin_fmaf(s9, h23[1], b));
 }
 
 // sum_i q_i * x_i over the 8 codes of one dword (x in element order)
