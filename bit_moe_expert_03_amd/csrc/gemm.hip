@@ -38,6 +38,10 @@
 // operand, so the accumulators hold the transposed tile: register r of lane
 // l is D[row l % 32][column 8 (r / 4) + 4 (l / 32) + r % 4], one output row
 // per lane, which the epilogues store straight from registers.
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -104,6 +108,11 @@ struct BSrc {
     uint32_t soff;         // byte offset of this lane's scale/bias row (lane % 32)
     int kbytes;            // bytes of codes per row (K / 2)
     int ngroups;           // groups per row (K / G)
+    // chained column blocks (down GEMM): pair p belongs to column block
+    // p >> pshift; the wave's rows of column block c start c * cq code bytes
+    // and c * cs scale bytes after those of block 0.  pshift = 30: one block.
+    int pshift;
+    uint32_t cq, cs;
 };
 
 // Copy the codes of pair p (K steps 2p, 2p+1: 64 bytes per row) of this
@@ -113,7 +122,8 @@ struct BSrc {
 // window is clamped to the row.
 __device__ __forceinline__ uint32_t b_offset(const BSrc &src, int p)
 {
-    return src.qrow + min(64u * p + src.c16, (uint32_t)src.kbytes - 16u);
+    const uint32_t c = (uint32_t)p >> src.pshift, pp = (uint32_t)p & ((1u << src.pshift) - 1u);
+    return src.qrow + c * src.cq + min(64u * pp + src.c16, (uint32_t)src.kbytes - 16u);
 }
 
 __device__ __forceinline__ void b_dma(const BSrc &src, int p, uint8_t *wave_buf)
@@ -127,9 +137,11 @@ template <int G>
 __device__ __forceinline__ void sb_load(SBPair<G> &t, const BSrc &src, int p)
 {
     constexpr int NG = 128 / G;  // groups per pair
-    const int g0 = p * NG;
+    const uint32_t c = (uint32_t)p >> src.pshift;
+    const int g0 = (int)((uint32_t)p & ((1u << src.pshift) - 1u)) * NG;
+    const uint32_t off = src.soff + c * src.cs;
     auto at = [&](const uint16_t *base, int g) __attribute__((always_inline)) {
-        return reinterpret_cast<const uint8_t *>(base) + src.soff + 2 * g;
+        return reinterpret_cast<const uint8_t *>(base) + off + 2 * g;
     };
     if constexpr (G == 128) {
         t.s0[0] = *reinterpret_cast<const uint16_t *>(at(src.s0, g0));
@@ -317,17 +329,46 @@ struct Carry {
 // the 4 code copies issued after them need not; at J = 0 everything, which
 // includes the codes of pair p+1 that the end of the next step reads.  After
 // the barrier every wave's copies up to there are in LDS.
-template <int MS, int G, int ST>
-__device__ __forceinline__ void mainloop_step(int kt, int nk, int npair, const uint16_t *abase,
+// Steps of one main loop: nt K steps in npair pairs.  With chained column
+// blocks (nc > 1, steps per block nk a power of two) step kt multiplies the
+// A columns of K step kt & kmask into the weights of column block kt / nk.
+struct LoopShape {
+    int nt, npair, kmask, kshift;
+};
+
+// A chained loop's end of a column block: the epilogue stores the block's
+// accumulators (column block c), then they are cleared for the next one.
+struct NoEpilogue {
+    template <int MS>
+    __device__ __forceinline__ void operator()(int, f32x16 (&)[MS], f32x16 (&)[MS]) const {}
+};
+
+// One K step.  ST = kt % 6 fixes J = kt & 1 (A stage, step inside the pair)
+// and PB = (kt / 2) % 3 (B buffer of the pair).  Codes are copied two pairs
+// ahead, A one step ahead, scales one pair ahead (registers).  Issue order
+// at J = 0: the scale loads of pair p+1, then (spread over the sub-steps) the
+// copies of A(kt+1) and those of pair p+2 (into the buffer of pair p-1, last
+// read one step before this one); at J = 1 the copies of A(kt+1).  Entry
+// wait: at J = 1 the scales and this wave's copy of A(kt) must have landed,
+// the 4 code copies issued after them need not; at J = 0 everything, which
+// includes the codes of pair p+1 that the end of the next step reads.  After
+// the barrier every wave's copies up to there are in LDS.  A chained loop
+// stores a finished column block at the end of its last step (kt + 1 a
+// multiple of nk, always a J = 1 step); its stores are in the vector-memory
+// count, so the entry wait of the next step (J = 0: everything) also covers
+// them.
+template <int MS, int G, int ST, class Epi>
+__device__ __forceinline__ void mainloop_step(int kt, const LoopShape &ls, const uint16_t *abase,
                                               const uint32_t (&aoff)[MS], const BSrc &bsrc, const LdsBufs &L,
-                                              Carry<G> &cs, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
+                                              Carry<G> &cs, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS], const Epi &epi)
 {
     constexpr int J = ST & 1, PB = (ST >> 1) % 3;
     if constexpr (J == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
     block_sync();
-    if constexpr (J == 0) sb_load<G>(cs.sbn, bsrc, min((kt >> 1) + 1, npair - 1));
-    const StepCopies<MS, J == 0> cp = {abase + min(kt + 1, nk - 1) * kKStep, aoff, L.a<J ^ 1>(), bsrc,
-                                       b_offset(bsrc, min((kt >> 1) + 2, npair - 1)), L.b<(PB + 2) % 3>()};
+    if constexpr (J == 0) sb_load<G>(cs.sbn, bsrc, min((kt >> 1) + 1, ls.npair - 1));
+    const StepCopies<MS, J == 0> cp = {abase + (min(kt + 1, ls.nt - 1) & ls.kmask) * kKStep, aoff, L.a<J ^ 1>(),
+                                       bsrc, b_offset(bsrc, min((kt >> 1) + 2, ls.npair - 1)),
+                                       L.b<(PB + 2) % 3>()};
     // next step: same pair at J = 0, first step of the next pair at J = 1
     constexpr int PBN = J == 0 ? PB : (PB + 1) % 3;
     const StepCodes cur = cs.codes;
@@ -336,6 +377,15 @@ __device__ __forceinline__ void mainloop_step(int kt, int nk, int npair, const u
     kstep<MS, G, J == 0>(L.a<J>(), cur, sc, first, L.b<PBN>(), J == 0 ? cs.sb : cs.sbn, J ^ 1, cs.codes, cs.first,
                          acc0, acc1, cp);
     if constexpr (J == 1) cs.sb = cs.sbn;
+    if constexpr (J == 1 && !std::is_same<Epi, NoEpilogue>::value) {
+        if (((kt + 1) & ls.kmask) == 0) {
+            epi(kt >> ls.kshift, acc0, acc1);
+#pragma unroll
+            for (int i = 0; i < MS; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { acc0[i][r] = 0.f; acc1[i][r] = 0.f; }
+        }
+    }
 }
 
 // Main loop shared by both GEMMs: acc0 += A B0^T, acc1 += A B1^T over K for
@@ -343,12 +393,12 @@ __device__ __forceinline__ void mainloop_step(int kt, int nk, int npair, const u
 // 6 steps: the loop body is 6 straight-line steps, and 1 to 5 remaining
 // steps run the same instantiations under conditions.  Past the end, copies
 // re-load valid data instead of branching.
-template <int MS, int G>
-__device__ __forceinline__ void mainloop(const uint16_t *abase, const uint32_t (&aoff)[MS], int K, const BSrc &bsrc,
-                                         const LdsBufs &L, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS])
+template <int MS, int G, class Epi = NoEpilogue>
+__device__ __forceinline__ void mainloop(const uint16_t *abase, const uint32_t (&aoff)[MS], const LoopShape &ls,
+                                         const BSrc &bsrc, const LdsBufs &L, f32x16 (&acc0)[MS],
+                                         f32x16 (&acc1)[MS], const Epi &epi = Epi())
 {
-    const int nk = K / kKStep;
-    const int npair = (nk + 1) >> 1;
+    const int nk = ls.nt;
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
@@ -358,7 +408,7 @@ __device__ __forceinline__ void mainloop(const uint16_t *abase, const uint32_t (
     sb_load<G>(cs.sb, bsrc, 0);
     a_dma<MS>(abase, aoff, 0, L.a<0>());
     b_dma(bsrc, 0, L.b<0>());
-    b_dma(bsrc, min(1, npair - 1), L.b<1>());
+    b_dma(bsrc, min(1, ls.npair - 1), L.b<1>());
     wait_vmcnt<0>();
     block_sync();
     read_codes(L.b<0>(), 0, cs.codes);
@@ -366,19 +416,26 @@ __device__ __forceinline__ void mainloop(const uint16_t *abase, const uint32_t (
 
     int kt = 0;
     for (; kt + 5 < nk; kt += 6) {
-        mainloop_step<MS, G, 0>(kt, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
-        mainloop_step<MS, G, 1>(kt + 1, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
-        mainloop_step<MS, G, 2>(kt + 2, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
-        mainloop_step<MS, G, 3>(kt + 3, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
-        mainloop_step<MS, G, 4>(kt + 4, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
-        mainloop_step<MS, G, 5>(kt + 5, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+        mainloop_step<MS, G, 0>(kt, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        mainloop_step<MS, G, 1>(kt + 1, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        mainloop_step<MS, G, 2>(kt + 2, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        mainloop_step<MS, G, 3>(kt + 3, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        mainloop_step<MS, G, 4>(kt + 4, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        mainloop_step<MS, G, 5>(kt + 5, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
     }
-    if (kt < nk) mainloop_step<MS, G, 0>(kt, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
-    if (kt + 1 < nk) mainloop_step<MS, G, 1>(kt + 1, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
-    if (kt + 2 < nk) mainloop_step<MS, G, 2>(kt + 2, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
-    if (kt + 3 < nk) mainloop_step<MS, G, 3>(kt + 3, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
-    if (kt + 4 < nk) mainloop_step<MS, G, 4>(kt + 4, nk, npair, abase, aoff, bsrc, L, cs, acc0, acc1);
+    if (kt < nk) mainloop_step<MS, G, 0>(kt, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+    if (kt + 1 < nk) mainloop_step<MS, G, 1>(kt + 1, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+    if (kt + 2 < nk) mainloop_step<MS, G, 2>(kt + 2, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+    if (kt + 3 < nk) mainloop_step<MS, G, 3>(kt + 3, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+    if (kt + 4 < nk) mainloop_step<MS, G, 4>(kt + 4, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
     wait_vmcnt<0>();  // no copy into LDS outlives the loop
+}
+
+// the shape of a loop over one column block of K (no chaining)
+__device__ __forceinline__ LoopShape single_block_loop(int K)
+{
+    const int nk = K / kKStep;
+    return {nk, (nk + 1) >> 1, 0x7fffffff, 30};
 }
 
 // Byte offsets from the A base of this lane's source (row, chunk) for the A
@@ -429,8 +486,9 @@ __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int r
     src.soff = (uint32_t)(lane & 31) * Kg * 2u;
     src.kbytes = Kq;
     src.ngroups = Kg;
+    src.pshift = 30; src.cq = 0; src.cs = 0;
     f32x16 accg[MS], accu[MS];
-    mainloop<MS, G>(a.x, aoff, a.d, src, L, accg, accu);
+    mainloop<MS, G>(a.x, aoff, single_block_loop(a.d), src, L, accg, accu);
     // epilogue: h = bf16(silu(g) * u), one row per lane, 16-byte stores
     if (ncol0 < N) {
 #pragma unroll
@@ -489,10 +547,38 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gateup_kernel(GateUpArgs 
         gateup_body<1, G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
 }
 
-template <int MS, int G>
+// Store 64 columns (this wave's share of a 256-column block) of the tile's
+// rows: o = w_route * acc as bf16, one row per lane, 16-byte stores.
+template <int MS>
+__device__ __forceinline__ void down_store(const DownArgs &a, const float (&wrow)[MS], int rows, int orow0,
+                                           int ncol0, const f32x16 (&acc0)[MS], const f32x16 (&acc1)[MS])
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+        const int m = 32 * i + (lane & 31);
+        if (m >= rows) continue;
+        uint16_t *orow = a.obuf + (size_t)(orow0 + m) * a.d + ncol0;
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = wrow[i] * acc0[i][r];
+        store_row32(orow, v);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = wrow[i] * acc1[i][r];
+        store_row32(orow + 32, v);
+    }
+}
+
+// Down GEMM over one tile and NC = a.nc consecutive 256-column blocks
+// starting at block nt0.  CHAIN (NC > 1): one continuous pipeline over
+// NC x (K / 64) steps -- the h tile is the A operand of every column block,
+// the codes and scales move to the next block's rows, and each finished
+// block is stored from inside the loop, so the block's prologue (tile
+// lookup, routing weights, first copies) is paid once per NC blocks.
+template <int MS, int G, bool CHAIN>
 __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows, int K,
                                           const moe_qmat &m, size_t ebase, const uint16_t *hsrc,
-                                          int orow0, bool routed, int nt, uint8_t *lds_a0,
+                                          int orow0, bool routed, int nt0, uint8_t *lds_a0,
                                           uint8_t *lds_a1, uint8_t *lds_b0, uint8_t *lds_b1, uint8_t *lds_b2)
 {
     const int lane = threadIdx.x & 63;
@@ -507,7 +593,7 @@ __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows,
     const LdsBufs L = {lds_a0, lds_a1, lds_b0 + wslice, lds_b1 + wslice, lds_b2 + wslice};
     uint32_t aoff[MS];
     a_offsets<MS>(aoff, K, nullptr, 1, row0, rows);
-    const int ncol0 = nt * 256 + 64 * wave;  // this wave: columns [ncol0, ncol0 + 64)
+    const int ncol0 = nt0 * 256 + 64 * wave;  // this wave: columns [ncol0, ncol0 + 64) of the first block
     const int nbase = ncol0 < a.d ? ncol0 : 0;  // idle waves compute on valid rows
     const int Kq = K >> 1, Kg = K / G;
     BSrc src;
@@ -522,22 +608,23 @@ __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows,
     src.kbytes = Kq;
     src.ngroups = Kg;
     f32x16 acc0[MS], acc1[MS];
-    mainloop<MS, G>(hsrc, aoff, K, src, L, acc0, acc1);
-    // epilogue: o = w_route * acc as bf16, one row per lane, 16-byte stores
-    if (ncol0 < a.d) {
-#pragma unroll
-        for (int i = 0; i < MS; ++i) {
-            const int m = 32 * i + (lane & 31);
-            if (m >= rows) continue;
-            uint16_t *orow = a.obuf + (size_t)(orow0 + m) * a.d + ncol0;
-            float v[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) v[r] = wrow[i] * acc0[i][r];
-            store_row32(orow, v);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) v[r] = wrow[i] * acc1[i][r];
-            store_row32(orow + 32, v);
-        }
+    if constexpr (CHAIN) {
+        // steps per column block: a power of two (host-checked), so pairs
+        // never straddle two blocks
+        const int nk = K / kKStep;
+        const int kshift = 31 - __builtin_clz(nk);
+        src.pshift = kshift - 1;
+        src.cq = 256u * (uint32_t)Kq;
+        src.cs = 256u * (uint32_t)Kg * 2u;
+        const LoopShape ls = {nk * a.nc, nk * a.nc / 2, nk - 1, kshift};
+        auto epi = [&](int c, auto &r0, auto &r1) __attribute__((always_inline)) {
+            down_store<MS>(a, wrow, rows, orow0, ncol0 + 256 * c, r0, r1);
+        };
+        mainloop<MS, G>(hsrc, aoff, ls, src, L, acc0, acc1, epi);
+    } else {
+        src.pshift = 30; src.cq = 0; src.cs = 0;
+        mainloop<MS, G>(hsrc, aoff, single_block_loop(K), src, L, acc0, acc1);
+        if (ncol0 < a.d) down_store<MS>(a, wrow, rows, orow0, ncol0, acc0, acc1);
     }
 }
 
@@ -549,7 +636,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b2[kBBuf];
-    const int nblk_r = max(0, min(*a.tiles.num_tiles, a.tiles.max_tiles)) * a.ntn;  // routed blocks with work
+    const int ncb = a.ntn / a.nc;  // blocks per tile, each over a.nc column blocks
+    const int nblk_r = max(0, min(*a.tiles.num_tiles, a.tiles.max_tiles)) * ncb;  // routed blocks with work
     const int L = xcd_logical_block(blockIdx.x, nblk_r + a.nblk_s);
     if (L < 0) return;
     int row0, rows, K, nt;
@@ -559,8 +647,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     int orow0;  // first output row in obuf
     bool routed;
     if (L < nblk_r) {
-        const int tile = L / a.ntn;
-        nt = L - tile * a.ntn;
+        const int tile = L / ncb;
+        nt = (L - tile * ncb) * a.nc;
         ebase = (size_t)a.tiles.tile_expert[tile] * a.d;
         row0 = a.tiles.tile_row0[tile];
         rows = a.tiles.tile_rows[tile];
@@ -568,8 +656,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
         orow0 = row0;
         routed = true;
     } else {
-        const int tile = (L - nblk_r) / a.ntn;
-        nt = (L - nblk_r) - tile * a.ntn;
+        const int tile = (L - nblk_r) / ncb;
+        nt = ((L - nblk_r) - tile * ncb) * a.nc;
         row0 = tile * BM;
         rows = min(BM, a.T - row0);
         ebase = 0;
@@ -578,12 +666,21 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
         routed = false;
     }
     const int msub = (rows + 31) >> 5;
-    if (BM >= 128 && msub > 2)
-        down_body<(BM >= 128 ? 4 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
-    else if (BM >= 64 && msub == 2)
-        down_body<(BM >= 64 ? 2 : 1), G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
-    else
-        down_body<1, G>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+    if (a.nc > 1) {
+        if (BM >= 128 && msub > 2)
+            down_body<(BM >= 128 ? 4 : 1), G, true>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+        else if (BM >= 64 && msub == 2)
+            down_body<(BM >= 64 ? 2 : 1), G, true>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+        else
+            down_body<1, G, true>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+    } else {
+        if (BM >= 128 && msub > 2)
+            down_body<(BM >= 128 ? 4 : 1), G, false>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+        else if (BM >= 64 && msub == 2)
+            down_body<(BM >= 64 ? 2 : 1), G, false>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+        else
+            down_body<1, G, false>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+    }
 }
 
 // one wave per token: 16-byte loads of the k routed rows and the shared row
@@ -635,6 +732,26 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__rest
     }
 }
 
+// Column blocks per down-GEMM block (chaining, see down_body): only where
+// every wave has columns in every block (d a multiple of 256) and the steps
+// of a block (F / 64 = Fs / 64) are a power of two.  Two per block where the
+// grid still holds two rounds of blocks (2 per CU) at the largest tile
+// count: measured on the T = 4096 and T = 32768 workloads, 4 and 8 were no
+// faster than 2 (-3% and -8% down-GEMM time against 1).  The environment
+// variable MOE_DOWN_NC (a divisor of d / 256) overrides the choice for
+// tests and tuning.
+static int down_chain(const Plan &p, int BM, int ntn)
+{
+    const int nk = p.F / kKStep;
+    if (p.d % 256 != 0 || p.F != p.Fs || nk < 2 || (nk & (nk - 1)) != 0) return 1;
+    if (const char *e = getenv("MOE_DOWN_NC")) {
+        const int v = atoi(e);
+        if (v >= 1 && ntn % v == 0) return v;
+    }
+    const int64_t tiles = (p.A + BM - 1) / BM + (p.T + BM - 1) / BM;
+    return (ntn % 2 == 0 && tiles * (ntn / 2) >= 2 * 512) ? 2 : 1;
+}
+
 template <int BM, int G>
 static hipError_t launch_bm(const Plan &p, const uint16_t *x, const moe_weights &w,
                             const moe_routing &r, uint16_t *y, void *ws, hipStream_t s,
@@ -665,9 +782,10 @@ static hipError_t launch_bm(const Plan &p, const uint16_t *x, const moe_weights 
     dn.down = w.down; dn.sdown = w.sdown;
     dn.tiles = tiles;
     dn.ntn = (p.d + 255) / 256;
+    dn.nc = down_chain(p, BM, dn.ntn);
     dn.obuf = obuf;
-    dn.nblk_s = shared_tiles * dn.ntn;
-    dn.nblk_pad = ((int)p.max_tiles * dn.ntn + dn.nblk_s + 7) & ~7;
+    dn.nblk_s = shared_tiles * (dn.ntn / dn.nc);
+    dn.nblk_pad = ((int)p.max_tiles * (dn.ntn / dn.nc) + dn.nblk_s + 7) & ~7;
     launch(tr, moe_down_kernel<BM, G>, dim3(dn.nblk_pad), dim3(kGemmThreads), 0, s, dn);
 
     launch(tr, moe_combine_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, (const uint16_t *)obuf,

@@ -36,6 +36,7 @@ struct DownArgs {
     moe_qmat down, sdown;
     GemmTiles tiles;
     int ntn;                // 256-column blocks (d / 256, rounded up)
+    int nc;                 // column blocks per block (chained), divides ntn
     int nblk_s, nblk_pad;   // as in GateUpArgs
     uint16_t *obuf;         // [T*k + T][d] weighted outputs: sorted routed rows, then shared
 };

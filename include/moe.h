@@ -153,7 +153,11 @@ MOE_API moe_status moe_route(const moe_dims *dims, const float *logits, const mo
  * -> y bf16 [T][d].  Grouped GEMMs over the block map with the 4-bit weights
  * decoded inside the kernel (T >= 2), or matrix-vector kernels for T == 1.
  * `w` and `r` are host pointers to structs of device pointers; ws must not
- * be shared with a concurrently running call. */
+ * be shared with a concurrently running call.  Tuning override, read at each
+ * call: the environment variable MOE_DOWN_NC (a divisor of d / 256) sets how
+ * many 256-column blocks of a tile one down-GEMM workgroup runs as one
+ * pipeline, where d is a multiple of 256 and F = Fs = 64 * 2^n; it changes
+ * the schedule only, never the result. */
 MOE_API moe_status moe_ffn(const moe_dims *dims, const uint16_t *x, const moe_weights *w,
                    const moe_routing *r, uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 

@@ -159,6 +159,40 @@ def test_layer_full_size_sampled(name):
     check_y(c, g, ref, tokens=sample_tokens(c, ref))
 
 
+# Down GEMM with chained column blocks (one block runs several 256-column
+# blocks of its tile as one pipeline): forced through the MOE_DOWN_NC tuning
+# override on shapes with d a multiple of 256 and F = Fs = 64 * 2^n.
+CHAINED = {
+    "chain_T300_d1024_F128": wl.Dims(T=300, d=1024, E=16, k=4, F=128, Fs=128, G=64),
+    "chain_T90_d1024_F256_G32": wl.Dims(T=90, d=1024, E=8, k=2, F=256, Fs=256, G=32),
+    "chain_T40_d512_F512_G128": wl.Dims(T=40, d=512, E=4, k=3, F=512, Fs=512, G=128),
+}
+
+
+@pytest.mark.parametrize("nc", [2, 4])
+@pytest.mark.parametrize("name", list(CHAINED))
+def test_down_chained_column_blocks(name, nc, monkeypatch):
+    dims = CHAINED[name]
+    if (dims.d // 256) % nc:
+        pytest.skip("chain length must divide the column-block count")
+    monkeypatch.setenv("MOE_DOWN_NC", str(nc))
+    c = wl.make_case(dims, seed=200 + list(CHAINED).index(name))
+    for tile_m in (0, 32, 128):
+        g = run(c, tile_m=tile_m)
+        ref = check_routing(c, g)
+        check_y(c, g, ref)
+
+
+@pytest.mark.parametrize("nc", [1, 2, 8])
+def test_down_chain_lengths_full_size(nc, monkeypatch):
+    """T = 4096 Zipf at every chain length (the default picks one)."""
+    monkeypatch.setenv("MOE_DOWN_NC", str(nc))
+    c = wl.make_case("c3_prefill4096_zipf")
+    g = run(c)
+    ref = check_routing(c, g)
+    check_y(c, g, ref, tokens=sample_tokens(c, ref, n_random=16, seed=nc))
+
+
 GATED = ["ragged_T37_E16_k4", "T300_E16_k4_G64", "T70_E8_k3_G128", "T1_small_decode", "zipf_T500_E64_k6"]
 
 
