@@ -75,8 +75,11 @@ moe_status make_plan(const moe_dims *dm, Plan *p, const char **why)
     p->off_hr = off;   off = align_up(off + (size_t)p->A * d.F * 2);
     p->off_hs = off;   off = align_up(off + (size_t)d.T * d.Fs * 2);
     p->off_obuf = off; off = align_up(off + (size_t)(p->A + d.T) * d.d * 2);
-    p->off_dech = off; off = align_up(off + (size_t)(d.k + 1) * Fmax * 4);
-    p->off_gamma = off; off = align_up(off + 4);  // decode: the shared expert's gate value
+    // decode path (batches of at most kMaxDecodeT tokens): h per token and slot,
+    // the shared expert's gate value per token
+    const int td = d.T < 1 ? 1 : (d.T < kMaxDecodeT ? d.T : kMaxDecodeT);
+    p->off_dech = off; off = align_up(off + (size_t)td * (d.k + 1) * Fmax * 4);
+    p->off_gamma = off; off = align_up(off + (size_t)kMaxDecodeT * 4);
     p->ws_bytes = off;
     return MOE_OK;
 }
@@ -188,6 +191,13 @@ MOE_API moe_status moe_route(const moe_dims *dims, const float *logits, const mo
     return hip_status(launch_route(p, logits, *out, ws, (hipStream_t)stream), "moe_route launch");
 }
 
+// Batches of 1..kMaxDecodeT tokens run the matrix-vector kernels of the
+// decode path (each token streams its experts' rows; no tiles to fill).
+static bool decode_batch(const Plan &p)
+{
+    return p.T >= 1 && p.T <= kMaxDecodeT && p.A <= kMaxDecodeAssign;
+}
+
 MOE_API moe_status moe_ffn(const moe_dims *dims, const uint16_t *x, const moe_weights *w,
                            const moe_routing *r, uint16_t *y, void *ws, size_t ws_bytes, void *stream)
 {
@@ -200,14 +210,14 @@ MOE_API moe_status moe_ffn(const moe_dims *dims, const uint16_t *x, const moe_we
     if ((st = check_weights(p, w)) || (st = check_routing(p, r))) return st;
     if (p.T == 0) return MOE_OK;
     (void)hipGetLastError();
-    hipError_t e = (p.T == 1) ? launch_decode(p, nullptr, x, *w, *r, y, ws, (hipStream_t)stream)
-                              : launch_ffn_gemm(p, x, *w, *r, y, ws, (hipStream_t)stream);
+    hipError_t e = decode_batch(p) ? launch_decode(p, nullptr, x, *w, *r, y, ws, (hipStream_t)stream)
+                                   : launch_ffn_gemm(p, x, *w, *r, y, ws, (hipStream_t)stream);
     return hip_status(e, "moe_ffn launch");
 }
 
 static int layer_kernels(const Plan &p)
 {
-    if (p.T == 1) return 2;              // decode gate/up, decode down
+    if (decode_batch(p)) return 2;       // decode gate/up, decode down
     if (p.T == 0) return 1;              // empty routing
     return 3 + 3;                        // route topk, scan, scatter; gate/up, down, combine
 }
@@ -229,7 +239,7 @@ static moe_status layer_impl(const moe_dims *dims, const float *logits, const ui
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     hipError_t e;
-    if (p.T == 1) {
+    if (decode_batch(p)) {
         e = launch_decode(p, logits, x, *w, *out, y, ws, s, tr);
     } else {
         e = launch_route(p, logits, *out, ws, s, tr);

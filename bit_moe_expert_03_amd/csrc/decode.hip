@@ -6,10 +6,16 @@
 // Lily Beats MLX-LM by 1.35x Running Qwen3.6 on Apple Silicon", section "Why
 // prefill and decode get different treatment").
 //
+// The same two kernels serve batches of up to kMaxDecodeT tokens (the
+// pages' few-token verify passes): every work wave and down block belongs to
+// one token, and an expert chosen by several tokens is streamed once per
+// token (the repeats mostly hit L2 / Infinity Cache).
+//
 // Two kernels per layer:
-//   decode_gateup_kernel  block 0: top-k + softmax of the token's logits and
-//                         the routing outputs, and the shared expert's gate
-//                         value when it is gated.  Every other wave owns
+//   decode_gateup_kernel  block 0: top-k + softmax of every token's logits
+//                         and the routing outputs (sorted order, counts,
+//                         offsets, block map), and the shared expert's gate
+//                         values when it is gated.  Every other wave owns
 //                         P (gate, up) row pairs of one expert slot
 //                         and writes h_j[n] = bf16(silu(W_gate,j[n] . x) *
 //                         (W_up,j[n] . x)).  A wave of routed slot j needs
@@ -40,17 +46,18 @@ namespace moe {
 constexpr int kDecThreads = 256;  // 4 waves per block
 constexpr int kDownRows = 2;      // output rows per down block
 constexpr int kDownMaxThreads = 512;
+constexpr int kMaxDecodeA = kMaxDecodeAssign;  // assignments of a batch
 
 struct DecodeArgs {
-    const float *logits;  // [1][E] or null (routing given in r)
-    const uint16_t *x;    // [1][d]
+    const float *logits;  // [T][E] or null (routing given in r)
+    const uint16_t *x;    // [T][d]
     moe_weights w;
     moe_routing r;
-    int d, E, k, F, Fs, G, Fmax;
+    int T, d, E, k, F, Fs, G, Fmax, tile_m;
     int wps_r, wps_s;     // work waves per routed slot, for the shared expert
-    uint16_t *h;          // [k+1][Fmax] bf16 workspace: slots 0..k-1 routed, k shared
-    float *gamma;         // workspace: weight of the shared expert (gated variant)
-    uint16_t *y;          // [1][d]
+    uint16_t *h;          // [T][k+1][Fmax] bf16 workspace: slots 0..k-1 routed, k shared
+    float *gamma;         // [T] workspace: weight of the shared expert (gated variant)
+    uint16_t *y;          // [T][d]
 };
 
 // ---- packed 4-bit dot products ---------------------------------------------
@@ -109,41 +116,86 @@ __device__ __forceinline__ float chunk_term(float dq128, const VecChunk &v, uint
 
 // ---- routing -----------------------------------------------------------------
 
-// routing outputs of the single token: ids, weights, the one-row-per-expert
-// histogram, its scan, the sorted order and the tiles
+// Routing outputs of the batch from the chosen ids and weights of its
+// A = T k assignments (a = t k + j): per-expert counts, their exclusive scan
+// (offsets) and the scan of the used-expert flags (tile index) by wave 0,
+// then the stable sorted position of each assignment, offsets[e] plus the
+// number of earlier assignments of the same expert.  An expert is chosen at
+// most once per token, so it has at most T <= tile_m rows and one tile.
 __device__ void decode_write_routing(const DecodeArgs &a, const int *s_ids, const float *s_w)
 {
+    __shared__ int cnt[kMaxE], off[kMaxE + 1], tix[kMaxE + 1];
     const int tid = threadIdx.x;
     const moe_routing &r = a.r;
-    for (int j = tid; j < a.k; j += blockDim.x) {
-        r.topk_ids[j] = s_ids[j];
-        r.topk_w[j] = s_w[j];
-        int rank = 0;  // sorted position = number of chosen experts with a lower id
-        for (int i = 0; i < a.k; ++i) rank += s_ids[i] < s_ids[j];
-        r.perm[rank] = j;
-        r.inv_perm[j] = rank;
-        r.tile_expert[rank] = s_ids[j];
-        r.tile_row0[rank] = rank;
-        r.tile_rows[rank] = 1;
+    const int A = a.T * a.k;
+    for (int e = tid; e < kMaxE; e += blockDim.x) {
+        int hit = 0;
+        if (e < a.E)
+            for (int i = 0; i < A; ++i) hit += s_ids[i] == e;
+        cnt[e] = hit;
     }
+    __syncthreads();
+    if (tid < kWave) {  // exclusive scans over the (at most 256) experts, 4 per lane
+        int v[4], u[4], sv = 0, su = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = cnt[4 * tid + i];
+            u[i] = v[i] > 0;
+            sv += v[i];
+            su += u[i];
+        }
+        int iv = sv, iu = su;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int x = __shfl_up(iv, o, kWave), y = __shfl_up(iu, o, kWave);
+            if (tid >= o) { iv += x; iu += y; }
+        }
+        int rv = iv - sv, ru = iu - su;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            off[4 * tid + i] = rv;
+            tix[4 * tid + i] = ru;
+            rv += v[i];
+            ru += u[i];
+        }
+        if (tid == kWave - 1) { off[kMaxE] = rv; tix[kMaxE] = ru; }
+    }
+    __syncthreads();
     for (int e = tid; e <= a.E; e += blockDim.x) {
-        int below = 0, hit = 0;
-        for (int i = 0; i < a.k; ++i) { below += s_ids[i] < e; hit += s_ids[i] == e; }
-        if (e < a.E) r.counts[e] = hit;
-        r.offsets[e] = below;
+        const int o = e < a.E ? off[e] : A;
+        r.offsets[e] = o;
+        if (e < a.E) {
+            r.counts[e] = cnt[e];
+            if (cnt[e]) {
+                r.tile_expert[tix[e]] = e;
+                r.tile_row0[tix[e]] = o;
+                r.tile_rows[tix[e]] = cnt[e];
+            }
+        } else {
+            *r.num_tiles = tix[kMaxE];
+        }
     }
-    if (tid == 0) *r.num_tiles = a.k;
+    for (int i = tid; i < A; i += blockDim.x) {
+        const int e = s_ids[i];
+        int rank = off[e];
+        for (int i2 = 0; i2 < i; ++i2) rank += s_ids[i2] == e;
+        r.topk_ids[i] = e;
+        r.topk_w[i] = s_w[i];
+        r.perm[rank] = i;
+        r.inv_perm[i] = rank;
+    }
 }
 
-// block 0 of the gate/up grid: top-k, softmax over the k chosen logits
+// block 0 of the gate/up grid: top-k, softmax over the k chosen logits of
+// each token (wave w takes tokens w, w + 4, ...)
 __device__ void decode_routing_block(const DecodeArgs &a)
 {
-    __shared__ int s_ids[kMaxE];
-    __shared__ float s_w[kMaxE];
+    __shared__ int s_ids[kMaxDecodeA];
+    __shared__ float s_w[kMaxDecodeA];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (wave == 0) {
+    for (int t = wave; t < a.T; t += kDecThreads / kWave) {
         TopK tk;
-        wave_topk(load_logits(a.logits, a.E), a.E, a.k, tk);
+        wave_topk(load_logits(a.logits + (size_t)t * a.E, a.E), a.E, a.k, tk);
         float ex[4], part = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -155,34 +207,38 @@ __device__ void decode_routing_block(const DecodeArgs &a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int j = lane + 64 * c;
-            if (j < a.k) { s_ids[j] = tk.id[c]; s_w[j] = ex[c] * inv; }
+            if (j < a.k) { s_ids[t * a.k + j] = tk.id[c]; s_w[t * a.k + j] = ex[c] * inv; }
         }
     }
     __syncthreads();
     decode_write_routing(a, s_ids, s_w);
 }
 
-// block 0 of the gate/up grid, gated shared expert: gamma = sigmoid(x . g)
+// block 0 of the gate/up grid, gated shared expert: gamma_t = sigmoid(x_t . g)
 __device__ void decode_shared_gate(const DecodeArgs &a)
 {
     __shared__ float part[kDecThreads / kWave];
     const int tid = threadIdx.x;
-    float z = 0.f;
-    for (int c = tid * 8; c < a.d; c += kDecThreads * 8) {
-        const uint4 xv = *reinterpret_cast<const uint4 *>(a.x + c);
-        const uint4 gv = *reinterpret_cast<const uint4 *>(a.w.shared_gate + c);
-        z = dot2_bf16(xv.x, gv.x, z);
-        z = dot2_bf16(xv.y, gv.y, z);
-        z = dot2_bf16(xv.z, gv.z, z);
-        z = dot2_bf16(xv.w, gv.w, z);
-    }
-    z = wave_sum(z);
-    if ((tid & 63) == 0) part[tid >> 6] = z;
-    __syncthreads();
-    if (tid == 0) {
-        float t = 0.f;
-        for (int w = 0; w < kDecThreads / kWave; ++w) t += part[w];
-        *a.gamma = 1.0f / (1.0f + __expf(-t));
+    for (int t = 0; t < a.T; ++t) {
+        const uint16_t *xt = a.x + (size_t)t * a.d;
+        float z = 0.f;
+        for (int c = tid * 8; c < a.d; c += kDecThreads * 8) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(xt + c);
+            const uint4 gv = *reinterpret_cast<const uint4 *>(a.w.shared_gate + c);
+            z = dot2_bf16(xv.x, gv.x, z);
+            z = dot2_bf16(xv.y, gv.y, z);
+            z = dot2_bf16(xv.z, gv.z, z);
+            z = dot2_bf16(xv.w, gv.w, z);
+        }
+        z = wave_sum(z);
+        if ((tid & 63) == 0) part[tid >> 6] = z;
+        __syncthreads();
+        if (tid == 0) {
+            float v = 0.f;
+            for (int w = 0; w < kDecThreads / kWave; ++w) v += part[w];
+            a.gamma[t] = 1.0f / (1.0f + __expf(-v));
+        }
+        __syncthreads();
     }
 }
 
@@ -212,19 +268,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
         return;
     }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int gw = (blockIdx.x - 1) * (kDecThreads / kWave) + wave;  // work wave
+    const int per_token = a.k * a.wps_r + a.wps_s;  // work waves of one token
+    const int gw0 = (blockIdx.x - 1) * (kDecThreads / kWave) + wave;
+    const int t = gw0 / per_token;
+    if (t >= a.T) return;
+    const int gw = gw0 - t * per_token;  // work wave inside the token
     const int nchunk = a.d >> 5;
     int slot, n0;
     if (gw < a.k * a.wps_r) {
         slot = a.k - 1 - gw / a.wps_r;
         n0 = (gw % a.wps_r) * P;
-    } else if (gw < a.k * a.wps_r + a.wps_s) {
+    } else {
         slot = a.k;
         n0 = (gw - a.k * a.wps_r) * P;
-    } else {
-        return;
     }
     const bool shared = slot == a.k;
+    const uint16_t *xt = a.x + (size_t)t * a.d;
 
     // this lane's chunks of x: chunk c = lane + 64 i covers x[32c, 32c+32)
     uint4 xr[NCH][4];
@@ -232,7 +291,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
     for (int i = 0; i < NCH; ++i) {
         const int c = lane + 64 * i;
         if (c < nchunk) {
-            const uint4 *xp = reinterpret_cast<const uint4 *>(a.x + (size_t)c * 32);
+            const uint4 *xp = reinterpret_cast<const uint4 *>(xt + (size_t)c * 32);
 #pragma unroll
             for (int v = 0; v < 4; ++v) xr[i][v] = xp[v];
         }
@@ -247,12 +306,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
         int e;
         if (a.logits) {
             uint32_t key[4];
-            const LogitQuad lq = load_logits(a.logits, a.E);
+            const LogitQuad lq = load_logits(a.logits + (size_t)t * a.E, a.E);
 #pragma unroll
             for (int c = 0; c < 4; ++c) key[c] = (4 * lane + c < a.E) ? logit_key(lq.v[c]) : 0u;
             e = wave_rank_expert(key, slot);
         } else {
-            e = a.r.topk_ids[slot];
+            e = a.r.topk_ids[t * a.k + slot];
         }
         row0 = (size_t)e * a.F + n0;
     }
@@ -281,7 +340,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
             accu[pi] += chunk_term(dot_codes32(ru[pi][i].q, xv), xv, ru[pi][i].s, ru[pi][i].b);
         }
     }
-    uint16_t *hrow = a.h + (size_t)slot * a.Fmax + n0;
+    uint16_t *hrow = a.h + ((size_t)t * (a.k + 1) + slot) * a.Fmax + n0;
 #pragma unroll
     for (int pi = 0; pi < P; ++pi) {
         const float g = wave_sum(accg[pi]);
@@ -292,14 +351,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
 
 // ---- down ---------------------------------------------------------------------
 
-// One block = kDownRows output rows; lane chunks c = tid, tid + blockDim, ...
-// of [h_s, h_0 .. h_{k-1}] in 32-element chunks.
+// One block = kDownRows output rows of token blockIdx.y; lane chunks
+// c = tid, tid + blockDim, ... of [h_s, h_0 .. h_{k-1}] in 32-element chunks.
 __global__ __launch_bounds__(kDownMaxThreads) void decode_down_kernel(DecodeArgs a)
 {
     __shared__ float red[kDownMaxThreads / kWave][kDownRows];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nw = blockDim.x >> 6;
     const int row0 = blockIdx.x * kDownRows;
+    const int t = blockIdx.y;
     const int cF = a.F >> 5, cFs = a.Fs >> 5;
     const int nchunks = a.k * cF + cFs;
     float acc[kDownRows];
@@ -313,11 +373,11 @@ __global__ __launch_bounds__(kDownMaxThreads) void decode_down_kernel(DecodeArgs
         if (c < cFs) {  // shared expert: no routing needed
             j = a.k; f0 = c * 32; Fw = a.Fs; m = &a.w.sdown;
             ebase = 0;
-            wj = a.w.shared_gate ? *a.gamma : 1.0f;
+            wj = a.w.shared_gate ? a.gamma[t] : 1.0f;
         } else {
             j = (c - cFs) / cF; f0 = (c - cFs - j * cF) * 32; Fw = a.F; m = &a.w.down;
-            ebase = (size_t)a.r.topk_ids[j] * a.d;
-            wj = a.r.topk_w[j];
+            ebase = (size_t)a.r.topk_ids[t * a.k + j] * a.d;
+            wj = a.r.topk_w[t * a.k + j];
         }
         uint4 q[kDownRows];
         uint16_t s[kDownRows], b[kDownRows];
@@ -331,7 +391,7 @@ __global__ __launch_bounds__(kDownMaxThreads) void decode_down_kernel(DecodeArgs
             b[r] = m->b[gi];
         }
         uint4 hr[4];
-        const uint4 *hp = reinterpret_cast<const uint4 *>(a.h + (size_t)j * a.Fmax + f0);
+        const uint4 *hp = reinterpret_cast<const uint4 *>(a.h + ((size_t)t * (a.k + 1) + j) * a.Fmax + f0);
 #pragma unroll
         for (int v = 0; v < 4; ++v) hr[v] = hp[v];
         VecChunk hv;
@@ -348,7 +408,7 @@ __global__ __launch_bounds__(kDownMaxThreads) void decode_down_kernel(DecodeArgs
     if (tid < kDownRows && row0 + tid < a.d) {
         float v = 0.f;
         for (int w = 0; w < nw; ++w) v += red[w][tid];
-        a.y[row0 + tid] = f32_to_bf16(v);
+        a.y[(size_t)t * a.d + row0 + tid] = f32_to_bf16(v);
     }
 }
 
@@ -357,7 +417,7 @@ static void launch_gateup(EventTrace *tr, DecodeArgs &a, hipStream_t s)
 {
     a.wps_r = a.F / P;
     a.wps_s = a.Fs / P;
-    const int waves = a.k * a.wps_r + a.wps_s;
+    const int waves = a.T * (a.k * a.wps_r + a.wps_s);
     const int nb = 1 + (waves + kDecThreads / kWave - 1) / (kDecThreads / kWave);
     launch(tr, decode_gateup_kernel<NCH, P>, dim3(nb), dim3(kDecThreads), 0, s, a);
 }
@@ -371,7 +431,7 @@ hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
     a.x = x;
     a.w = w;
     a.r = r;
-    a.d = p.d; a.E = p.E; a.k = p.k; a.F = p.F; a.Fs = p.Fs; a.G = p.G;
+    a.T = p.T; a.d = p.d; a.E = p.E; a.k = p.k; a.F = p.F; a.Fs = p.Fs; a.G = p.G; a.tile_m = p.tile_m;
     a.Fmax = p.F > p.Fs ? p.F : p.Fs;
     a.h = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + p.off_dech);
     a.gamma = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_gamma);
@@ -390,7 +450,7 @@ hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
     int nw = (nchunks + kWave - 1) / kWave;
     nw = nw < 1 ? 1 : (nw > kDownMaxThreads / kWave ? kDownMaxThreads / kWave : nw);
     const int nb2 = (p.d + kDownRows - 1) / kDownRows;
-    launch(tr, decode_down_kernel, dim3(nb2), dim3(nw * kWave), 0, s, a);
+    launch(tr, decode_down_kernel, dim3(nb2, p.T), dim3(nw * kWave), 0, s, a);
     return hipGetLastError();
 }
 

@@ -13,6 +13,10 @@ namespace moe {
 
 constexpr int kRouteThreads = 1024;  // routing kernels: 16 waves per block
 constexpr int kMaxE = 256;
+// batches of up to kMaxDecodeT tokens (and at most kMaxDecodeAssign token-
+// expert assignments) take the matrix-vector kernels of the decode path
+constexpr int kMaxDecodeT = 8;
+constexpr int kMaxDecodeAssign = 512;
 
 // Everything derived from moe_dims that the launchers need.
 struct Plan {

@@ -151,7 +151,10 @@ MOE_API moe_status moe_route(const moe_dims *dims, const float *logits, const mo
 
 /* Expert FFN: x bf16 [T][d] + weights + routing (as produced by moe_route)
  * -> y bf16 [T][d].  Grouped GEMMs over the block map with the 4-bit weights
- * decoded inside the kernel (T >= 2), or matrix-vector kernels for T == 1.
+ * decoded inside the kernel, or, for small batches (1 <= T <= 8 and T*k <= 512:
+ * single-token decode and the pages' few-token verify passes, section "What
+ * failed" of "Perplexity's Lily Beats MLX-LM by 1.35x Running Qwen3.6 on Apple
+ * Silicon"), matrix-vector kernels that stream each token's expert rows.
  * `w` and `r` are host pointers to structs of device pointers; ws must not
  * be shared with a concurrently running call.  Tuning override, read at each
  * call: the environment variable MOE_DOWN_NC (a divisor of d / 256) sets how
@@ -161,17 +164,18 @@ MOE_API moe_status moe_route(const moe_dims *dims, const float *logits, const mo
 MOE_API moe_status moe_ffn(const moe_dims *dims, const uint16_t *x, const moe_weights *w,
                    const moe_routing *r, uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 
-/* moe_route followed by moe_ffn.  For T == 1 the routing is computed inside
- * the decode kernels (every field of *out is still written). */
+/* moe_route followed by moe_ffn.  For small batches (1 <= T <= 8 and
+ * T*k <= 512) the routing is computed inside the matrix-vector kernels (every
+ * field of *out is still written, identical to moe_route's). */
 MOE_API moe_status moe_layer(const moe_dims *dims, const float *logits, const uint16_t *x,
                      const moe_weights *w, const moe_routing *out, uint16_t *y,
                      void *ws, size_t ws_bytes, void *stream);
 
 /* Host-only, pure.  Number of kernels one moe_layer call launches for these
- * dims, in launch order: T == 1: decode gate/up (with routing), decode down;
- * T >= 2: route top-k, route scan, route scatter, gate/up GEMM, down GEMM
- * (routed and shared rows), combine; T == 0: empty routing.  0 for invalid
- * dims. */
+ * dims, in launch order: small batches (1 <= T <= 8, T*k <= 512): decode
+ * gate/up (with routing), decode down; larger T: route top-k, route scan,
+ * route scatter, gate/up GEMM, down GEMM (routed and shared rows), combine;
+ * T == 0: empty routing.  0 for invalid dims. */
 MOE_API int32_t moe_layer_kernels(const moe_dims *dims);
 
 /* Measurement form of moe_layer: identical work; kernel i is launched with

@@ -111,3 +111,13 @@ def test_null_pointers_and_small_workspace_are_rejected():
     q = B.moe_qmat(_fake_ptr(60), _fake_ptr(61), _fake_ptr(62))
     assert L.moe_dequant(ctypes.byref(q), 4, 64, 48, _fake_ptr(63), None) == B.MOE_ERR_SHAPE
     assert L.moe_dequant(ctypes.byref(q), 4, 48, 32, _fake_ptr(63), None) == B.MOE_ERR_SHAPE
+
+
+def test_small_batches_take_the_two_decode_kernels():
+    """1 <= T <= 8 with T*k <= 512: two kernels (decode gate/up with routing,
+    decode down); larger batches: three routing kernels and three GEMM-path
+    kernels."""
+    base = dict(d=256, E=128, F=128, Fs=128, G=64)
+    for T, k, n in [(1, 8, 2), (2, 8, 2), (8, 8, 2), (8, 64, 2), (9, 8, 6), (8, 65, 6), (4096, 8, 6), (0, 8, 1)]:
+        dm = B.make_dims(wl.Dims(T=T, k=k, **base))
+        assert B.moe_layer_kernels(dm) == n, (T, k)

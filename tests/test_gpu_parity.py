@@ -26,6 +26,10 @@ SMALL = {
     "T2_smallest_gemm": (wl.Dims(T=2, d=128, E=8, k=2, F=64, Fs=64, G=32), False),
     "zipf_T500_E64_k6": (wl.Dims(T=500, d=128, E=64, k=6, F=64, Fs=64, G=32), True),
     "T1_small_decode": (wl.Dims(T=1, d=256, E=16, k=4, F=128, Fs=192, G=64), False),
+    # small batches (2 <= T <= 8, T k <= 512) take the matrix-vector kernels
+    "T5_small_batch": (wl.Dims(T=5, d=256, E=16, k=4, F=128, Fs=192, G=64), False),
+    "T8_k64_batch_limit": (wl.Dims(T=8, d=128, E=64, k=64, F=64, Fs=64, G=32), False),
+    "T8_k65_over_limit": (wl.Dims(T=8, d=128, E=80, k=65, F=64, Fs=64, G=32), False),
     # many rows per expert: pairs of full 128-row tiles (256-row super-tiles),
     # widths that are not multiples of 128 and odd K-step counts
     "T1000_E4_k2_pairs": (wl.Dims(T=1000, d=128, E=4, k=2, F=192, Fs=64, G=64), False),
@@ -193,7 +197,8 @@ def test_down_chain_lengths_full_size(nc, monkeypatch):
     check_y(c, g, ref, tokens=sample_tokens(c, ref, n_random=16, seed=nc))
 
 
-GATED = ["ragged_T37_E16_k4", "T300_E16_k4_G64", "T70_E8_k3_G128", "T1_small_decode", "zipf_T500_E64_k6"]
+GATED = ["ragged_T37_E16_k4", "T300_E16_k4_G64", "T70_E8_k3_G128", "T1_small_decode", "T5_small_batch",
+         "zipf_T500_E64_k6"]
 
 
 @pytest.mark.parametrize("name", GATED)
@@ -240,6 +245,34 @@ def test_decode_tie_heavy_logits(seed):
     rng = np.random.default_rng(seed)
     L = rng.integers(-1, 2, (1, dims.E)).astype(np.float32)
     L[0, rng.random(dims.E) < 0.3] = -0.0
+    c["logits"] = L
+    for mode in ("layer", "split"):
+        g = run(c, mode=mode)
+        ref = check_routing(c, g)
+        check_y(c, g, ref)
+
+
+@pytest.mark.parametrize("T", [2, 3, 5, 8])
+def test_small_batch_full_size(T):
+    """Few-token batches at the workload's layer shape: every token of every
+    slot, routing outputs bit-exact in both the fused and the split call."""
+    dims = wl.Dims(T=T, d=2048, E=256, k=8, F=512, Fs=512, G=64)
+    c = wl.make_case(dims, seed=400 + T, index=T)
+    for mode in ("layer", "split"):
+        g = run(c, mode=mode)
+        ref = check_routing(c, g)
+        check_y(c, g, ref)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_small_batch_tie_heavy_logits(seed):
+    """T = 6, logits in {-1, -0, 0, 1}: tokens share experts and tie inside
+    the top 8, so the batch's stable sorted order and tiles are exercised."""
+    dims = wl.Dims(T=6, d=256, E=32, k=8, F=128, Fs=128, G=64)
+    c = wl.make_case(dims, seed=500 + seed)
+    rng = np.random.default_rng(50 + seed)
+    L = rng.integers(-1, 2, (dims.T, dims.E)).astype(np.float32)
+    L[rng.random((dims.T, dims.E)) < 0.3] = -0.0
     c["logits"] = L
     for mode in ("layer", "split"):
         g = run(c, mode=mode)
@@ -306,7 +339,7 @@ def test_expert_relabelling_leaves_y_unchanged():
 
 # ------------------------------------------------------------------ launch forms
 
-@pytest.mark.parametrize("name", ["c0_tiny", "T1_small_decode"])
+@pytest.mark.parametrize("name", ["c0_tiny", "T1_small_decode", "T5_small_batch"])
 def test_timed_entry_point_matches_and_times(name):
     c = _case(name)
     dims = c["dims"]
@@ -331,7 +364,7 @@ def test_timed_entry_point_matches_and_times(name):
                           [e.cuda_event for e in evs[:-1]])
 
 
-@pytest.mark.parametrize("name", ["c0_tiny", "T1_small_decode", "T300_E16_k4_G64"])
+@pytest.mark.parametrize("name", ["c0_tiny", "T1_small_decode", "T5_small_batch", "T300_E16_k4_G64"])
 def test_graph_replays_match_eager(name):
     c = _case(name)
     dims = c["dims"]
