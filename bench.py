@@ -243,9 +243,32 @@ def bench_decode(B, wl, args):
     }
     log(f"decode: {value:.0f} tok/s, {out['ms_per_step'] * 1e3:.2f} us/step, gate/up {gu_ms * 1e3:.2f} us "
         f"({achieved:.0f} GB/s), down {per_kernel[1] * 1e3:.2f} us")
+    out["small_batches"] = bench_small_batches(B, wl, args, dims, seed, sets)
     del sets, calls
     torch.cuda.empty_cache()
     return out, (dims, host_sets, host_inputs)
+
+
+def bench_small_batches(B, wl, args, dims, seed, sets):
+    """Context, not the metric: few-token batches (the verify passes of
+    speculative decoding) at the decode layer shape over the same rotated
+    weight sets, one graph of args.steps // 4 layer calls per batch size."""
+    import torch
+    out = {}
+    steps = max(8, args.steps // 4)
+    for T in (2, 4, 8):
+        dT = dims.replace(T=T)
+        dm = B.make_dims(dT)
+        calls = []
+        for s in range(len(sets)):
+            c = wl.make_case(dT, seed=seed, index=1000 + 40 * T + s, weights=False)
+            y = torch.empty((T, dims.d), dtype=torch.int16, device="cuda")
+            calls.append((to_dev(c["logits"]), to_dev(c["x"]), sets[s][1], y))
+        sec, per_kernel = run_timed(B, dm, calls, steps, 8)
+        out[f"T{T}"] = {"tokens_per_s": T * steps / sec, "us_per_step": sec * 1e6 / steps,
+                        "per_kernel_us": [k * 1e3 for k in per_kernel]}
+        log(f"small batch T={T}: {sec * 1e6 / steps:.1f} us/step, {T * steps / sec:.0f} tok/s")
+    return out
 
 
 def bench_prefill(B, wl, args):
@@ -377,7 +400,7 @@ def main():
                                "40 layer weight sets rotated per step", "T": 1, "weight_sets": 40},
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
-        "decode_detail": {k: dec[k] for k in ("per_kernel_ms", "layer_bytes", "layer_gbs")},
+        "decode_detail": {k: dec[k] for k in ("per_kernel_ms", "layer_bytes", "layer_gbs", "small_batches")},
         "prefill": pre,
         "achievable": peaks,
     }
