@@ -683,7 +683,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     }
 }
 
-// one wave per token: 16-byte loads of the k routed rows and the shared row
+// One wave per token: 16-byte loads of the k routed rows and the shared row.
+// The row indices are read once, with every lane active (lane j of register
+// g holds inv_perm[t k + 64 g + j]), and taken out lane by lane with
+// v_readlane on those registers, so the row loads of a pass do not wait on
+// index loads.  The column passes are wave-uniform (loads and stores are
+// predicated on c < d) and each index is clamped to the routed rows, so a
+// corrupt routing input cannot send a load outside obuf.  Each lane sums 8
+// columns per pass in slot order (fp32), then the shared row.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__restrict__ obuf,
                                                           const int32_t *__restrict__ inv_perm,
                                                           int T, int k, int d,
@@ -693,8 +700,15 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__rest
 {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (t >= T) return;
+    if (t >= T) return;  // wave-uniform
     const int64_t shared_row = (int64_t)T * k + t;
+    const uint32_t last_routed = (uint32_t)(T * k - 1);
+    int myrow[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int j = 64 * g + lane;
+        myrow[g] = j < k ? inv_perm[(int64_t)t * k + j] : 0;
+    }
     float gamma = 1.0f;  // weight of the shared expert's row
     if (shared_gate) {
         float z = 0.f;
@@ -708,27 +722,47 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__rest
         }
         gamma = 1.0f / (1.0f + __expf(-wave_sum(z)));
     }
-    for (int c = lane * 8; c < d; c += 64 * 8) {
+    for (int c0 = 0; c0 < d; c0 += 64 * 8) {  // wave-uniform passes
+        const int c = c0 + lane * 8;
+        const bool act = c < d;
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-        for (int j = 0; j <= k; ++j) {
-            const int64_t row = (j < k) ? (int64_t)inv_perm[(int64_t)t * k + j] : shared_row;
-            const float wr = (j < k) ? 1.0f : gamma;
-            const uint4 v = *reinterpret_cast<const uint4 *>(obuf + row * d + c);
+        auto add = [&](const uint4 &v, float wr) __attribute__((always_inline)) {
             const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 acc[2 * i] += wr * bf16_to_f32(wd[i] & 0xFFFFu);
                 acc[2 * i + 1] += wr * bf16_to_f32(wd[i] >> 16);
             }
+        };
+        // slots in groups of 8: the 8 loads of a group are issued together
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;  // wave-uniform
+                const int l = j & 63, g = (j >> 6) & 3;
+                const int r0 = __builtin_amdgcn_readlane(myrow[0], l);
+                const int r1 = __builtin_amdgcn_readlane(myrow[1], l);
+                const int r2 = __builtin_amdgcn_readlane(myrow[2], l);
+                const int r3 = __builtin_amdgcn_readlane(myrow[3], l);
+                const uint32_t row = min((uint32_t)(g == 0 ? r0 : g == 1 ? r1 : g == 2 ? r2 : r3), last_routed);
+                if (j < k && act) v[u] = *reinterpret_cast<const uint4 *>(obuf + (int64_t)row * d + c);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (j0 + u < k && act) add(v[u], 1.0f);
         }
-        uint4 o;
-        o.x = pack_bf16x2(acc[0], acc[1]);
-        o.y = pack_bf16x2(acc[2], acc[3]);
-        o.z = pack_bf16x2(acc[4], acc[5]);
-        o.w = pack_bf16x2(acc[6], acc[7]);
-        *reinterpret_cast<uint4 *>(y + (int64_t)t * d + c) = o;
+        if (act) {
+            add(*reinterpret_cast<const uint4 *>(obuf + shared_row * d + c), gamma);
+            uint4 o;
+            o.x = pack_bf16x2(acc[0], acc[1]);
+            o.y = pack_bf16x2(acc[2], acc[3]);
+            o.z = pack_bf16x2(acc[4], acc[5]);
+            o.w = pack_bf16x2(acc[6], acc[7]);
+            *reinterpret_cast<uint4 *>(y + (int64_t)t * d + c) = o;
+        }
     }
 }
 
