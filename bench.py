@@ -243,7 +243,7 @@ def bench_decode(B, wl, args):
     }
     log(f"decode: {value:.0f} tok/s, {out['ms_per_step'] * 1e3:.2f} us/step, gate/up {gu_ms * 1e3:.2f} us "
         f"({achieved:.0f} GB/s), down {per_kernel[1] * 1e3:.2f} us")
-    out["small_batches"] = bench_small_batches(B, wl, args, dims, seed, sets)
+    out["small_batches"] = None if args.no_small_batches else bench_small_batches(B, wl, args, dims, seed, sets)
     del sets, calls
     torch.cuda.empty_cache()
     return out, (dims, host_sets, host_inputs)
@@ -351,6 +351,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-small-batches", action="store_true",
+                    help="skip the few-token batch context (counter passes keep the decode kernels at T=1)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="first run a plain copy kernel of this many MB (scale for counter passes)")

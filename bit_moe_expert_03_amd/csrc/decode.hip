@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
             for (int c = 0; c < 4; ++c) key[c] = (4 * lane + c < a.E) ? logit_key(lq.v[c]) : 0u;
             e = wave_rank_expert(key, slot);
         } else {
-            e = a.r.topk_ids[t * a.k + slot];
+            e = min((uint32_t)a.r.topk_ids[t * a.k + slot], (uint32_t)(a.E - 1));  // ids from the caller: kept in range
         }
         row0 = (size_t)e * a.F + n0;
     }
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kDownMaxThreads) void decode_down_kernel(DecodeArgs
             wj = a.w.shared_gate ? a.gamma[t] : 1.0f;
         } else {
             j = (c - cFs) / cF; f0 = (c - cFs - j * cF) * 32; Fw = a.F; m = &a.w.down;
-            ebase = (size_t)a.r.topk_ids[t * a.k + j] * a.d;
+            ebase = (size_t)min((uint32_t)a.r.topk_ids[t * a.k + j], (uint32_t)(a.E - 1)) * a.d;
             wj = a.r.topk_w[t * a.k + j];
         }
         uint4 q[kDownRows];

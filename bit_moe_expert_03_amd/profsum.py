@@ -40,12 +40,25 @@ def source_hash(paths) -> str:
 
 
 def trace_rows(db_path):
-    """(name, calls, avg_us, min_us, max_us, total_us) per kernel name, by total time."""
+    """(name, calls, avg_us, min_us, max_us, total_us) per kernel and launch
+    shape, by total time.  A kernel launched with several grid shapes (the
+    decode kernels at T = 1 and at few-token batches) gets one row per shape,
+    its name suffixed with the grid in workgroups."""
     con = sqlite3.connect(db_path)
-    rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
-                       "from kernels group by name order by sum(duration) desc").fetchall()
+    rows = con.execute("select name, grid_x, grid_y, grid_z, workgroup_x, workgroup_y, workgroup_z, count(*), "
+                       "avg(duration), min(duration), max(duration), sum(duration) "
+                       "from kernels group by name, grid_x, grid_y, grid_z, workgroup_x, workgroup_y, workgroup_z "
+                       "order by sum(duration) desc").fetchall()
     con.close()
-    return [(r[0], r[1], r[2] / 1e3, r[3] / 1e3, r[4] / 1e3, r[5] / 1e3) for r in rows]
+    shapes = collections.Counter(r[0] for r in rows)
+    out = []
+    for r in rows:
+        name = r[0]
+        if shapes[name] > 1:
+            g = [max(1, r[i] // max(1, r[i + 3])) for i in (1, 2, 3)]
+            name = f"{short_name(name)} [grid {g[0]}x{g[1]}x{g[2]}]"
+        out.append((name, r[7], r[8] / 1e3, r[9] / 1e3, r[10] / 1e3, r[11] / 1e3))
+    return out
 
 
 def short_name(name: str) -> str:
@@ -78,7 +91,8 @@ def cmd_trace(a):
     print("| kernel | calls | avg us | min us | max us | total us |")
     print("|---|---|---|---|---|---|")
     for name, n, avg, mn, mx, tot in rows:
-        print(f"| `{short_name(name)[:90]}` | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {tot:.1f} |")
+        label = name if "[grid" in name else short_name(name)
+        print(f"| `{label[:110]}` | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {tot:.1f} |")
 
 
 def cmd_traffic(a):

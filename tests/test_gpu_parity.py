@@ -187,6 +187,19 @@ def test_down_chained_column_blocks(name, nc, monkeypatch):
         check_y(c, g, ref)
 
 
+def test_down_chain_length_does_not_change_bits(monkeypatch):
+    """The chain length changes the schedule only: each output element sees
+    the same MFMA sequence, so y is bit-identical for every length."""
+    dims = CHAINED["chain_T300_d1024_F128"]
+    c = wl.make_case(dims, seed=210)
+    ys = {}
+    for nc in (1, 2, 4):
+        monkeypatch.setenv("MOE_DOWN_NC", str(nc))
+        ys[nc] = run(c)["y_bits"]
+    np.testing.assert_array_equal(ys[1], ys[2])
+    np.testing.assert_array_equal(ys[1], ys[4])
+
+
 @pytest.mark.parametrize("nc", [1, 2, 8])
 def test_down_chain_lengths_full_size(nc, monkeypatch):
     """T = 4096 Zipf at every chain length (the default picks one)."""
