@@ -62,6 +62,7 @@ def _declare(lib):
     lib.oracle_block_map.restype = ctypes.c_int
     lib.oracle_ffn.argtypes = [ctypes.c_int] * 7 + [_U16P, ctypes.POINTER(_OWeights), _U16P, _I32P, _F64P,
                                                     _I32P, ctypes.c_int, ctypes.c_int, _F64P]
+    lib.oracle_router_logits.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _U16P, _F32P, _F32P, _F64P]
     return lib
 
 
@@ -153,6 +154,21 @@ def route(logits: np.ndarray, k: int, tile_m: int, max_tiles: Optional[int] = No
     te, tr, tn = block_map(counts, offsets, tile_m, max_tiles, lib)
     return {"ids": ids, "w": w, "counts": counts, "offsets": offsets, "perm": perm, "inv_perm": inv,
             "tile_expert": te, "tile_row0": tr, "tile_rows": tn, "num_tiles": len(te)}
+
+
+def router_logits(x_bits: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray] = None,
+                  lib=None) -> np.ndarray:
+    """fp64 router logits x W_r (+ bias): x bf16 bits [T][d], W_r fp32 [d][E]."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    W = np.ascontiguousarray(w_router, dtype=np.float32)
+    T, d = x.shape
+    E = W.shape[1]
+    assert W.shape[0] == d
+    L = np.empty((T, E), np.float64)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    lib.oracle_router_logits(T, d, E, _p(x, _U16P), _p(W, _F32P), None if b is None else _p(b, _F32P), _p(L, _F64P))
+    return L
 
 
 def ffn(dims, x_bits: np.ndarray, weights: dict, ids: np.ndarray, w: np.ndarray,

@@ -19,7 +19,11 @@
  *    page "Perplexity Open Sources Lily: Rust & Metal Engine for Qwen3.6",
  *    paragraph on the 70 GB -> 19.4 GB quantisation);
  *  - every expert is a SwiGLU MLP, o = W_down (silu(W_gate x) * (W_up x)),
- *    and the layer output is sum_j w_j o_j + o_shared.
+ *    and the layer output is sum_j w_j o_j + o_shared;
+ *  - the router scores each token against every expert: logits = x W_r
+ *    (+ a per-expert bias), W_r fp32 [d][E] (the step before the routing on
+ *    the same page, section "What Lily actually does": each token's router
+ *    picks its experts).
  *
  * Readings of what the pages leave open (each is pinned by a CPU test):
  *  - top-k order: larger logit first, ties to the lower expert id, -0 == +0;
@@ -275,4 +279,19 @@ void oracle_ffn(int T, int d, int E, int k, int F, int Fs, int G, const uint16_t
         free(h);
         free(o);
     }
+}
+
+/* Router logits: L[t][e] = sum_i x[t][i] W[i][e] (+ bias[e]), x bf16 [T][d],
+ * W fp32 [d][E], bias fp32 [E] or NULL, fp64 sums in input order. */
+void oracle_router_logits(int T, int d, int E, const uint16_t *x, const float *W, const float *bias,
+                          double *L)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += bf16_value(x[(size_t)t * d + i]) * (double)W[(size_t)i * E + e];
+            if (bias) acc += (double)bias[e];
+            L[(size_t)t * E + e] = acc;
+        }
 }

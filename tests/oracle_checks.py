@@ -317,9 +317,36 @@ def check_ffn_shared_gate(lib):
     np.testing.assert_allclose(y_half, 0.5 * (y_one + y_zero), rtol=1e-12, atol=1e-12)
 
 
+def check_router_logits_vs_matmul(lib):
+    """Router logits against numpy's fp64 matrix product of the decoded
+    activations (d != E, so a transposed operand shows) plus the bias."""
+    rng = np.random.default_rng(31)
+    T, d, E = 5, 96, 40
+    x = wl.to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    W = (rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)
+    bias = rng.standard_normal(E).astype(np.float32)
+    ref = bf16_to_f64(x) @ W.astype(np.float64) + bias.astype(np.float64)
+    got = oracle.router_logits(x, W, bias, lib=lib)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    got0 = oracle.router_logits(x, W, None, lib=lib)
+    np.testing.assert_allclose(got0, ref - bias.astype(np.float64), rtol=1e-12, atol=1e-12)
+
+
+def check_router_logits_identity(lib):
+    """Closed form: with W_r the first E columns of the identity (d >= E),
+    token t's logits are its first E activations, exactly."""
+    rng = np.random.default_rng(32)
+    T, d, E = 3, 64, 48
+    x = wl.to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    W = np.eye(d, E, dtype=np.float32)
+    got = oracle.router_logits(x, W, None, lib=lib)
+    assert np.array_equal(got, bf16_to_f64(x)[:, :E])
+
+
 ALL_CHECKS = [
     check_packing_fixture, check_rounding_fixture, check_dequant_closed_form,
     check_dequant_general_rounding, check_route_fixture, check_topk_vs_argsort,
     check_weights_special, check_counting_sort, check_block_map, check_ffn_bruteforce,
     check_ffn_single_expert_torch, check_ffn_integer, check_ffn_metamorphic, check_ffn_shared_gate,
+    check_router_logits_vs_matmul, check_router_logits_identity,
 ]

@@ -32,6 +32,8 @@ MUTATIONS = [
     ("routing_weight_dropped", "yt[i] += w[(size_t)t * k + j] * o[i];", "yt[i] += o[i];"),
     ("down_transposed", "weight_at(down, Fw, G, i, n)", "weight_at(down, Fw, G, n % d, i % Fw)"),
     ("x_index", "xt[i] = bf16_value(x[(size_t)t * d + i]);", "xt[i] = bf16_value(x[(size_t)t + i]);"),
+    ("router_transposed", "(double)W[(size_t)i * E + e]", "(double)W[((size_t)e * d + i) % ((size_t)d * E)]"),
+    ("router_bias_dropped", "if (bias) acc += (double)bias[e];", "if (bias) acc += 0.0;"),
 ]
 
 
