@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_ERR_ARG, MOE_ERR_SHAPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 EXPORTS = ("moe_abi_version", "moe_tile_m", "moe_max_tiles", "moe_workspace_bytes", "moe_route",
            "moe_ffn", "moe_layer", "moe_layer_kernels", "moe_layer_timed", "moe_dequant",
+           "moe_router_packed_bytes", "moe_router_pack", "moe_route_x",
            "moe_status_string", "moe_last_error")
 MATS = ("gate", "up", "down", "sgate", "sup", "sdown")
 
@@ -65,7 +66,7 @@ def lib():
         for f in ("moe_tile_m", "moe_layer_kernels"):
             getattr(L, f).restype = ctypes.c_int32
             getattr(L, f).argtypes = [P(moe_dims)]
-        for f in ("moe_max_tiles", "moe_workspace_bytes"):
+        for f in ("moe_max_tiles", "moe_workspace_bytes", "moe_router_packed_bytes"):
             getattr(L, f).restype = ctypes.c_size_t
             getattr(L, f).argtypes = [P(moe_dims)]
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
@@ -75,7 +76,10 @@ def lib():
         L.moe_layer_timed.argtypes = [P(moe_dims), vp, vp, P(moe_weights), P(moe_routing), vp, vp, sz,
                                       vp, P(ctypes.c_void_p), ctypes.c_int32]
         L.moe_dequant.argtypes = [P(moe_qmat), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
-        for f in ("moe_route", "moe_ffn", "moe_layer", "moe_layer_timed", "moe_dequant"):
+        L.moe_router_pack.argtypes = [P(moe_dims), vp, vp, vp]
+        L.moe_route_x.argtypes = [P(moe_dims), vp, vp, vp, vp, P(moe_routing), vp, sz, vp]
+        for f in ("moe_route", "moe_ffn", "moe_layer", "moe_layer_timed", "moe_dequant", "moe_router_pack",
+                  "moe_route_x"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -165,6 +169,23 @@ def moe_route(dims: moe_dims, logits: torch.Tensor, routing: Dict[str, torch.Ten
     r = routing_struct(routing)
     _check(lib().moe_route(ctypes.byref(dims), _ptr(logits), ctypes.byref(r), _ptr(ws),
                            ws.numel(), _stream(stream)))
+
+
+def moe_router_packed_bytes(dims: moe_dims) -> int:
+    return lib().moe_router_packed_bytes(ctypes.byref(dims))
+
+
+def moe_router_pack(dims: moe_dims, w_router: torch.Tensor, packed: torch.Tensor, stream=None):
+    """w_router fp32 [d][E] -> packed bf16 hi/lo router (moe_router_packed_bytes bytes)."""
+    _check(lib().moe_router_pack(ctypes.byref(dims), _ptr(w_router), _ptr(packed), _stream(stream)))
+
+
+def moe_route_x(dims: moe_dims, x: torch.Tensor, packed: torch.Tensor, bias: Optional[torch.Tensor],
+                logits: torch.Tensor, routing: Dict[str, torch.Tensor], ws: torch.Tensor, stream=None):
+    """Router logits x W_r (+ bias) into `logits`, then the routing into `routing`."""
+    r = routing_struct(routing)
+    _check(lib().moe_route_x(ctypes.byref(dims), _ptr(x), _ptr(packed), _ptr(bias), _ptr(logits),
+                             ctypes.byref(r), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def moe_ffn(dims: moe_dims, x: torch.Tensor, weights, routing: Dict[str, torch.Tensor],

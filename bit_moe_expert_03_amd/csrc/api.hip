@@ -80,6 +80,9 @@ moe_status make_plan(const moe_dims *dm, Plan *p, const char **why)
     const int td = d.T < 1 ? 1 : (d.T < kMaxDecodeT ? d.T : kMaxDecodeT);
     p->off_dech = off; off = align_up(off + (size_t)td * (d.k + 1) * Fmax * 4);
     p->off_gamma = off; off = align_up(off + (size_t)kMaxDecodeT * 4);
+    // router GEMM: partial logits of its K ranges (only when it splits K)
+    const int ks = router_splits(d.T, d.d, d.E);
+    p->off_router = off; off = align_up(off + (ks > 1 ? (size_t)ks * d.T * d.E * 4 : 0));
     p->ws_bytes = off;
     return MOE_OK;
 }
@@ -189,6 +192,50 @@ MOE_API moe_status moe_route(const moe_dims *dims, const float *logits, const mo
     if ((st = check_routing(p, out))) return st;
     (void)hipGetLastError();
     return hip_status(launch_route(p, logits, *out, ws, (hipStream_t)stream), "moe_route launch");
+}
+
+MOE_API size_t moe_router_packed_bytes(const moe_dims *dims)
+{
+    Plan p;
+    const char *why;
+    if (make_plan(dims, &p, &why) != MOE_OK) return 0;
+    return (size_t)2 * router_epad(p.E) * p.d * 2;
+}
+
+MOE_API moe_status moe_router_pack(const moe_dims *dims, const float *w_router, uint16_t *packed, void *stream)
+{
+    Plan p;
+    const char *why = "";
+    moe_status st = make_plan(dims, &p, &why);
+    if (st != MOE_OK) return fail(st, "%s", why);
+    const size_t wb = (size_t)p.d * p.E * 4, pb = (size_t)2 * router_epad(p.E) * p.d * 2;
+    if (!ptr_ok(w_router, wb)) return fail(MOE_ERR_ARG, "w_router: null or misaligned pointer");
+    if (!ptr_ok(packed, pb)) return fail(MOE_ERR_ARG, "packed: null or misaligned pointer");
+    if (overlap(w_router, wb, packed, pb)) return fail(MOE_ERR_ARG, "w_router and packed overlap");
+    (void)hipGetLastError();
+    return hip_status(launch_router_pack(w_router, p.d, p.E, packed, (hipStream_t)stream), "moe_router_pack launch");
+}
+
+MOE_API moe_status moe_route_x(const moe_dims *dims, const uint16_t *x, const uint16_t *packed, const float *bias,
+                               float *logits, const moe_routing *out, void *ws, size_t ws_bytes, void *stream)
+{
+    Plan p;
+    moe_status st = common(dims, &p, ws, ws_bytes);
+    if (st) return st;
+    const size_t xb = (size_t)p.T * p.d * 2, lb = (size_t)p.T * p.E * 4;
+    const size_t pb = (size_t)2 * router_epad(p.E) * p.d * 2;
+    if (!ptr_ok(x, xb)) return fail(MOE_ERR_ARG, "x: null or misaligned pointer");
+    if (!ptr_ok(packed, pb)) return fail(MOE_ERR_ARG, "packed: null or misaligned pointer");
+    if (!ptr_ok(logits, lb)) return fail(MOE_ERR_ARG, "logits: null or misaligned pointer");
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 3u)) return fail(MOE_ERR_ARG, "bias: misaligned pointer");
+    if (overlap(x, xb, logits, lb) || overlap(packed, pb, logits, lb))
+        return fail(MOE_ERR_ARG, "logits overlaps x or packed");
+    if ((st = check_routing(p, out))) return st;
+    (void)hipGetLastError();
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_router(p, x, packed, bias, logits, ws, s);
+    if (e == hipSuccess) e = launch_route(p, logits, *out, ws, s);
+    return hip_status(e, "moe_route_x launch");
 }
 
 // Batches of 1..kMaxDecodeT tokens run the matrix-vector kernels of the

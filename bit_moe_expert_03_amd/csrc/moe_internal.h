@@ -27,7 +27,7 @@ struct Plan {
     int route_nbp;      // route blocks rounded up to a multiple of 16 (histogram row pitch)
     int64_t max_tiles;  // length of the tile arrays
     // workspace carving (byte offsets)
-    size_t off_hist, off_hr, off_hs, off_obuf, off_dech, off_gamma, ws_bytes;
+    size_t off_hist, off_hr, off_hs, off_obuf, off_dech, off_gamma, off_router, ws_bytes;
 };
 
 // Optional per-kernel timing (measurement entry point): kernel i of a call
@@ -64,6 +64,13 @@ moe_status make_plan(const moe_dims *dims, Plan *p, const char **why);
 // ---- route.hip
 hipError_t launch_route(const Plan &p, const float *logits, const moe_routing &r, void *ws,
                         hipStream_t s, EventTrace *tr = nullptr);
+
+// ---- router.hip: logits = x W_r (+ bias) from the packed bf16 hi/lo router
+int router_epad(int E);                    // experts rounded up to 64 (packed rows)
+int router_splits(int T, int d, int E);    // K ranges of the router GEMM
+hipError_t launch_router_pack(const float *W, int d, int E, uint16_t *P, hipStream_t s);
+hipError_t launch_router(const Plan &p, const uint16_t *x, const uint16_t *P, const float *bias, float *logits,
+                         void *ws, hipStream_t s);
 
 // ---- gemm.hip (T >= 2 path)
 hipError_t launch_ffn_gemm(const Plan &p, const uint16_t *x, const moe_weights &w,

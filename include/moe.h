@@ -149,6 +149,28 @@ MOE_API size_t moe_workspace_bytes(const moe_dims *dims);
 MOE_API moe_status moe_route(const moe_dims *dims, const float *logits, const moe_routing *out,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* Host-only, pure.  Bytes of the packed router that moe_router_pack writes
+ * and moe_route_x reads: 2 * roundup(E, 64) * d bf16 values; 0 for invalid
+ * dims. */
+MOE_API size_t moe_router_packed_bytes(const moe_dims *dims);
+
+/* Router weights for moe_route_x, once per weight set: w_router fp32 [d][E]
+ * (device) -> packed (device, moe_router_packed_bytes): the bf16 pair
+ * hi = bf16(W), lo = bf16(W - hi), expert-major [2][roundup(E,64)][d], padding
+ * rows zero.  x W = x hi + x lo up to 2^-17 |W| per weight.  Asynchronous on
+ * `stream`; the caller owns both buffers. */
+MOE_API moe_status moe_router_pack(const moe_dims *dims, const float *w_router, uint16_t *packed, void *stream);
+
+/* Routing from the activations: logits fp32 [T][E] = x W_r (+ bias) on the
+ * bf16 matrix cores from the packed router (x bf16 [T][d]; bias fp32 [E] or
+ * NULL; fp32 accumulation, deterministic), written to `logits` (device,
+ * caller-owned), then the routing of moe_route on those logits into *out.
+ * The router computes each token's scores against every expert before its
+ * experts are picked (page "Perplexity's Lily Beats MLX-LM by 1.35x Running
+ * Qwen3.6 on Apple Silicon", section "What Lily actually does"). */
+MOE_API moe_status moe_route_x(const moe_dims *dims, const uint16_t *x, const uint16_t *packed, const float *bias,
+                               float *logits, const moe_routing *out, void *ws, size_t ws_bytes, void *stream);
+
 /* Expert FFN: x bf16 [T][d] + weights + routing (as produced by moe_route)
  * -> y bf16 [T][d].  Grouped GEMMs over the block map with the 4-bit weights
  * decoded inside the kernel, or, for small batches (1 <= T <= 8 and T*k <= 512:

@@ -121,3 +121,19 @@ def test_small_batches_take_the_two_decode_kernels():
     for T, k, n in [(1, 8, 2), (2, 8, 2), (8, 8, 2), (8, 64, 2), (9, 8, 6), (8, 65, 6), (4096, 8, 6), (0, 8, 1)]:
         dm = B.make_dims(wl.Dims(T=T, k=k, **base))
         assert B.moe_layer_kernels(dm) == n, (T, k)
+
+
+def test_router_packed_bytes_and_argument_checks():
+    """Packed router size: two bf16 matrices of roundup(E, 64) rows x d; the
+    router entry points reject null pointers before launching anything."""
+    dm = B.make_dims(wl.CONFIGS["c1_decode"])
+    assert B.moe_router_packed_bytes(dm) == 2 * 256 * 2048 * 2
+    dm16 = B.make_dims(wl.CONFIGS["c0_tiny"])
+    assert B.moe_router_packed_bytes(dm16) == 2 * 64 * 256 * 2
+    L = B.lib()
+    assert L.moe_router_pack(ctypes.byref(dm), None, None, None) == B.MOE_ERR_ARG
+    r = B.moe_routing()
+    assert L.moe_route_x(ctypes.byref(dm), None, None, None, None, ctypes.byref(r), None,
+                         B.moe_workspace_bytes(dm), None) == B.MOE_ERR_ARG
+    bad = B.make_dims(wl.CONFIGS["c1_decode"].replace(E=0))
+    assert B.moe_router_packed_bytes(bad) == 0

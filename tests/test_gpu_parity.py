@@ -405,3 +405,60 @@ def test_graph_replays_match_eager(name):
         # the program's own eager work between replays
         B.moe_layer(dm, lg, x, wdev, B.alloc_routing(dm), torch.empty_like(y), B.alloc_workspace(dm))
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ router projection
+
+def _route_x(c, with_bias):
+    """moe_router_pack + moe_route_x on the case's activations and router."""
+    dims = c["dims"]
+    dm = B.make_dims(dims)
+    wr = wl.make_router(dims, c["seed"])
+    bias = wl.zipf_bias(dims.E, c["seed"]).astype(np.float32) if with_bias else None
+    packed = torch.empty(B.moe_router_packed_bytes(dm) // 2, dtype=torch.int16, device="cuda")
+    B.moe_router_pack(dm, dev(wr), packed)
+    logits = torch.full((dims.T, dims.E), float("nan"), dtype=torch.float32, device="cuda")
+    r = B.alloc_routing(dm)
+    for t in r.values():
+        t.fill_(-7)
+    B.moe_route_x(dm, dev(c["x"]), packed, dev(bias) if bias is not None else None, logits, r,
+                  B.alloc_workspace(dm))
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in r.items()}
+    g["tile_m"], g["max_tiles"] = B.moe_tile_m(dm), B.moe_max_tiles(dm)
+    return logits.cpu().numpy(), g, wr, bias
+
+
+ROUTER_CASES = [("c0_tiny", False), ("c1_decode", False), ("c2_prefill512", False),
+                ("c3_prefill4096_zipf", True), ("ragged_T37_E16_k4", False), ("T5_small_batch", True),
+                ("T8_k65_over_limit", False)]
+
+
+@pytest.mark.parametrize("name,with_bias", ROUTER_CASES, ids=[n for n, _ in ROUTER_CASES])
+def test_route_x_logits_and_routing(name, with_bias):
+    """Router logits from the packed bf16 hi/lo router on the matrix cores:
+    within the bound of the split (|W - hi - lo| <= 2^-17 |W|) and of fp32
+    accumulation, 2^-14 sum_i |x_i W_ie| + 1e-6, against the fp64 oracle;
+    the routing of those logits bit-exact against the oracle's routing of
+    the same logits (near-ties may order differently from the fp64 logits,
+    so the routing is compared on the GPU's own)."""
+    c = dict(_case(name) if name in SMALL else wl.make_case(name, weights=False))
+    L, g, wr, bias = _route_x(c, with_bias)
+    L_ref = oracle.router_logits(c["x"], wr, bias)
+    bound = 2.0 ** -14 * (np.abs(bf16_to_f64(c["x"])) @ np.abs(wr.astype(np.float64))) + 1e-6
+    assert np.all(np.isfinite(L)), "unwritten logits"
+    assert np.all(np.abs(L - L_ref) <= bound), float(np.max(np.abs(L - L_ref) / bound))
+    check_routing(dict(c, logits=L), g)
+
+
+def test_route_x_then_ffn_matches_oracle():
+    """The layer from the activations: moe_route_x, then moe_ffn on its
+    routing, against the oracle's layer on the GPU's logits."""
+    c = dict(_case("T300_E16_k4_G64"))
+    L, g_route, wr, _ = _route_x(c, False)
+    c2 = dict(c, logits=L)
+    g = run(c2, mode="split")  # moe_route on the same logits, then moe_ffn
+    for k in ("topk_ids", "perm", "inv_perm", "counts", "offsets"):
+        np.testing.assert_array_equal(g[k], g_route[k])
+    ref = check_routing(c2, g)
+    check_y(c2, g, ref)
