@@ -462,3 +462,33 @@ def test_route_x_then_ffn_matches_oracle():
         np.testing.assert_array_equal(g[k], g_route[k])
     ref = check_routing(c2, g)
     check_y(c2, g, ref)
+
+
+def test_route_x_empty_batch():
+    """T = 0: nothing to project or route; the call succeeds and writes the
+    empty histogram and tile count."""
+    dims = wl.Dims(T=0, d=256, E=16, k=2, F=128, Fs=128, G=32)
+    dm = B.make_dims(dims)
+    packed = torch.zeros(B.moe_router_packed_bytes(dm) // 2, dtype=torch.int16, device="cuda")
+    r = B.alloc_routing(dm)
+    for t in r.values():
+        t.fill_(-7)
+    B.moe_route_x(dm, torch.empty((0, dims.d), dtype=torch.int16, device="cuda"), packed, None,
+                  torch.empty((0, dims.E), dtype=torch.float32, device="cuda"), r, B.alloc_workspace(dm))
+    torch.cuda.synchronize()
+    assert np.all(r["counts"].cpu().numpy() == 0)
+    assert np.all(r["offsets"].cpu().numpy() == 0)
+    assert int(r["num_tiles"].cpu()[0]) == 0
+
+
+def test_small_batch_gated_shared_expert_full_size():
+    """A 4-token batch at the workload's layer shape with the shared expert
+    gated by sigmoid(x_t . g) per token (block 0 forms the four gates)."""
+    dims = wl.Dims(T=4, d=2048, E=256, k=8, F=512, Fs=512, G=64)
+    c = dict(wl.make_case(dims, seed=404, index=4))
+    rng = np.random.default_rng(10)
+    c["shared_gate"] = wl.to_bf16_bits((rng.standard_normal(dims.d) / np.sqrt(dims.d)).astype(np.float32))
+    for mode in ("layer", "split"):
+        g = run(c, mode=mode)
+        ref = check_routing(c, g)
+        check_y(c, g, ref)
