@@ -55,7 +55,9 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+/* 1: route / ffn / layer; 2: optional gated shared expert (moe_weights.shared_gate);
+ * 3: moe_router_pack / moe_route_x / moe_router_packed_bytes. */
+#define MOE_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define MOE_API __attribute__((visibility("default")))

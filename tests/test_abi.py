@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = B.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert B.moe_abi_version() == 2
+    assert B.moe_abi_version() == 3
 
 
 def test_status_strings():
