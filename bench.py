@@ -304,7 +304,39 @@ def bench_prefill(B, wl, args):
     }
     log(f"prefill: {value / 1e6:.2f} M tok/s, {ms * 1e3:.1f} us/step, kernels "
         + ", ".join(f"{n} {t * 1e3:.1f}us" for n, t in zip(names, per_kernel)))
+    out["route_from_x"] = bench_route_x(B, wl, c, dm)
     return out, c
+
+
+def bench_route_x(B, wl, c, dm, reps=20):
+    """Context: routing from the activations (router projection on the GPU,
+    then the routing kernels) against routing from given logits, per call."""
+    import torch
+    dims = c["dims"]
+    wr = wl.make_router(dims, c["seed"])
+    bias = wl.zipf_bias(dims.E, c["seed"]).astype("float32")
+    packed = torch.empty(B.moe_router_packed_bytes(dm) // 2, dtype=torch.int16, device="cuda")
+    B.moe_router_pack(dm, to_dev(wr), packed)
+    x, bd, lg_in = to_dev(c["x"]), to_dev(bias), to_dev(c["logits"])
+    lg = torch.empty((dims.T, dims.E), dtype=torch.float32, device="cuda")
+    r = B.alloc_routing(dm)
+    ws = B.alloc_workspace(dm)
+    res = {}
+    for label, f in (("route_x_us", lambda: B.moe_route_x(dm, x, packed, bd, lg, r, ws)),
+                     ("route_us", lambda: B.moe_route(dm, lg_in, r, ws))):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        res[label] = e0.elapsed_time(e1) / reps * 1e3
+    res["router_tflops"] = 2.0 * 2 * dims.T * dims.d * dims.E / ((res["route_x_us"] - res["route_us"]) * 1e-6) / 1e12
+    log(f"prefill: routing from x {res['route_x_us']:.1f} us/call (from logits {res['route_us']:.1f})")
+    return res
 
 
 def cpu_baseline_decode(wl, host, seconds):
