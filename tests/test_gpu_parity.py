@@ -30,7 +30,7 @@ SMALL = {
     "T5_small_batch": (wl.Dims(T=5, d=256, E=16, k=4, F=128, Fs=192, G=64), False),
     "T8_k64_batch_limit": (wl.Dims(T=8, d=128, E=64, k=64, F=64, Fs=64, G=32), False),
     "T8_k65_over_limit": (wl.Dims(T=8, d=128, E=80, k=65, F=64, Fs=64, G=32), False),
-    # many rows per expert: pairs of full 128-row tiles (256-row super-tiles),
+    # many rows per expert: several full 128-row tiles per expert,
     # widths that are not multiples of 128 and odd K-step counts
     "T1000_E4_k2_pairs": (wl.Dims(T=1000, d=128, E=4, k=2, F=192, Fs=64, G=64), False),
     "T600_E2_k1_G128_pairs": (wl.Dims(T=600, d=256, E=2, k=1, F=128, Fs=128, G=128), False),
@@ -132,7 +132,7 @@ def test_layer_small_shapes_all_tokens(name):
 
 @pytest.mark.parametrize("name", [n for n in SMALL if SMALL[n][0].T >= 2])
 def test_layer_small_shapes_tile128(name):
-    """Every small shape with 128-row tiles (the 256-row super-tile kernels)."""
+    """Every small shape with 128-row tiles (the four-sub-tile GEMM bodies)."""
     c = _case(name)
     g = run(c, tile_m=128)
     ref = check_routing(c, g)
