@@ -31,7 +31,7 @@ class MoeError(RuntimeError):
 
 
 class moe_dims(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "E", "k", "F", "Fs", "G", "tile_m")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "E", "k", "F", "Fs", "G", "tile_m", "down_nc")]
 
 
 class moe_qmat(ctypes.Structure):
@@ -88,10 +88,11 @@ def lib():
     return _lib
 
 
-def make_dims(dims, tile_m: int = 0) -> moe_dims:
-    """moe_dims from any object with T, d, E, k, F, Fs, G attributes."""
+def make_dims(dims, tile_m: int = 0, down_nc: int = 0) -> moe_dims:
+    """moe_dims from any object with T, d, E, k, F, Fs, G attributes; tile_m
+    and down_nc are schedule fields (0: the library picks)."""
     return moe_dims(dims.T, dims.d, dims.E, dims.k, dims.F, dims.Fs, dims.G,
-                    getattr(dims, "tile_m", 0) or tile_m)
+                    getattr(dims, "tile_m", 0) or tile_m, down_nc)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -161,7 +162,8 @@ def alloc_routing(dims: moe_dims, device="cuda") -> Dict[str, torch.Tensor]:
 
 
 def alloc_workspace(dims: moe_dims, device="cuda") -> torch.Tensor:
-    return torch.empty(max(moe_workspace_bytes(dims), 256), dtype=torch.uint8, device=device)
+    """Workspace of moe_workspace_bytes(dims), zero-filled before first use."""
+    return torch.zeros(max(moe_workspace_bytes(dims), 256), dtype=torch.uint8, device=device)
 
 
 def moe_route(dims: moe_dims, logits: torch.Tensor, routing: Dict[str, torch.Tensor],

@@ -60,7 +60,16 @@ moe_status make_plan(const moe_dims *dm, Plan *p, const char **why)
         *why = "tile_m not in {0, 32, 64, 128}";
         return MOE_ERR_SHAPE;
     }
+    if (d.down_nc < 0 || d.down_nc > 64) { *why = "down_nc outside [0, 64]"; return MOE_ERR_SHAPE; }
+    if (d.down_nc > 1) {
+        const int nk = d.F / 64;
+        if (d.d % 256 != 0 || d.F != d.Fs || nk < 2 || (nk & (nk - 1)) != 0 || (d.d / 256) % d.down_nc != 0) {
+            *why = "down_nc > 1 needs d a multiple of 256, F = Fs = 64 * 2^n (n >= 1) and down_nc dividing d/256";
+            return MOE_ERR_SHAPE;
+        }
+    }
     p->T = d.T; p->d = d.d; p->E = d.E; p->k = d.k; p->F = d.F; p->Fs = d.Fs; p->G = d.G;
+    p->down_nc = d.down_nc;
     p->A = (int64_t)d.T * d.k;
     p->tile_m = d.tile_m ? d.tile_m : pick_tile_m(p->A, d.E);
     // route chunks: 16 tokens per route block (one per wave of the top-k kernel)

@@ -38,8 +38,6 @@
 // operand, so the accumulators hold the transposed tile: register r of lane
 // l is D[row l % 32][column 8 (r / 4) + 4 (l / 32) + r % 4], one output row
 // per lane, which the epilogues store straight from registers.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -442,10 +440,11 @@ __device__ __forceinline__ LoopShape single_block_loop(int K)
 // copies of sub-tiles < MS: copy i fills rows 8 (4 i + w) + lane / 8 of the
 // stage, 8 lanes per 128-byte row, and the lane in slot c of its row copies
 // chunk c ^ ((row >> 1) & 7).  Rows are gathered through perm (routed tiles)
-// or contiguous; rows past the tile's end repeat its last row.
+// (values clamped to the nassign assignments) or contiguous; rows past the
+// tile's end repeat its last row.
 template <int MS>
-__device__ __forceinline__ void a_offsets(uint32_t (&aoff)[MS], int ld, const int32_t *perm, int k, int row0,
-                                          int rows)
+__device__ __forceinline__ void a_offsets(uint32_t (&aoff)[MS], int ld, const int32_t *perm, int k, int nassign,
+                                          int row0, int rows)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -454,7 +453,7 @@ __device__ __forceinline__ void a_offsets(uint32_t (&aoff)[MS], int ld, const in
         const int row = 8 * (4 * i + wave) + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         const int m = min(row, rows - 1);
-        const int src = perm ? perm[row0 + m] / k : row0 + m;
+        const int src = perm ? perm_at(perm, row0 + m, nassign) / k : row0 + m;
         aoff[i] = (uint32_t)src * (uint32_t)ld * 2u + (uint32_t)c * 16u;
     }
 }
@@ -470,7 +469,7 @@ __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int r
     const int wslice = wave * kBWave;
     const LdsBufs L = {lds_a0, lds_a1, lds_b0 + wslice, lds_b1 + wslice, lds_b2 + wslice};
     uint32_t aoff[MS];
-    a_offsets<MS>(aoff, a.d, routed ? a.perm : nullptr, a.k, row0, rows);
+    a_offsets<MS>(aoff, a.d, routed ? a.perm : nullptr, a.k, a.T * a.k, row0, rows);
     const int ncol0 = nt * 128 + 32 * wave;  // first h column of this wave
     const int nbase = ncol0 < N ? ncol0 : 0;  // idle waves compute on valid rows
     const int Kq = a.d >> 1, Kg = a.d / G;
@@ -521,11 +520,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gateup_kernel(GateUpArgs 
     if (L < nblk_r) {
         const int tile = L / a.ntn_r;
         nt = L - tile * a.ntn_r;
-        const int e = a.tiles.tile_expert[tile];
-        row0 = a.tiles.tile_row0[tile];
-        rows = a.tiles.tile_rows[tile];
+        const TileInfo ti = read_tile(a.tiles, tile, a.E, a.T * a.k, BM);
+        row0 = ti.row0;
+        rows = ti.rows;
         N = a.F; mg = &a.gate; mu = &a.up;
-        ebase = (size_t)e * a.F;
+        ebase = (size_t)ti.e * a.F;
         out = a.h_r;
         routed = true;
     } else {
@@ -587,12 +586,12 @@ __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows,
     float wrow[MS];
 #pragma unroll
     for (int i = 0; i < MS; ++i)
-        wrow[i] = routed ? a.topk_w[a.perm[row0 + min(32 * i + (lane & 31), rows - 1)]] : 1.0f;
+        wrow[i] = routed ? a.topk_w[perm_at(a.perm, row0 + min(32 * i + (lane & 31), rows - 1), a.T * a.k)] : 1.0f;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wslice = wave * kBWave;
     const LdsBufs L = {lds_a0, lds_a1, lds_b0 + wslice, lds_b1 + wslice, lds_b2 + wslice};
     uint32_t aoff[MS];
-    a_offsets<MS>(aoff, K, nullptr, 1, row0, rows);
+    a_offsets<MS>(aoff, K, nullptr, 1, 0, row0, rows);
     const int ncol0 = nt0 * 256 + 64 * wave;  // this wave: columns [ncol0, ncol0 + 64) of the first block
     const int nbase = ncol0 < a.d ? ncol0 : 0;  // idle waves compute on valid rows
     const int Kq = K >> 1, Kg = K / G;
@@ -649,9 +648,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     if (L < nblk_r) {
         const int tile = L / ncb;
         nt = (L - tile * ncb) * a.nc;
-        ebase = (size_t)a.tiles.tile_expert[tile] * a.d;
-        row0 = a.tiles.tile_row0[tile];
-        rows = a.tiles.tile_rows[tile];
+        const TileInfo ti = read_tile(a.tiles, tile, a.E, a.T * a.k, BM);
+        ebase = (size_t)ti.e * a.d;
+        row0 = ti.row0;
+        rows = ti.rows;
         K = a.F; m = &a.down; hsrc = a.h_r;
         orow0 = row0;
         routed = true;
@@ -771,17 +771,13 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__rest
 // of a block (F / 64 = Fs / 64) are a power of two.  Two per block where the
 // grid still holds two rounds of blocks (2 per CU) at the largest tile
 // count: measured on the T = 4096 and T = 32768 workloads, 4 and 8 were no
-// faster than 2 (-3% and -8% down-GEMM time against 1).  The environment
-// variable MOE_DOWN_NC (a divisor of d / 256) overrides the choice for
-// tests and tuning.
+// faster than 2 (-3% and -8% down-GEMM time against 1).  moe_dims.down_nc
+// (validated on the host) overrides the choice.
 static int down_chain(const Plan &p, int BM, int ntn)
 {
     const int nk = p.F / kKStep;
     if (p.d % 256 != 0 || p.F != p.Fs || nk < 2 || (nk & (nk - 1)) != 0) return 1;
-    if (const char *e = getenv("MOE_DOWN_NC")) {
-        const int v = atoi(e);
-        if (v >= 1 && ntn % v == 0) return v;
-    }
+    if (p.down_nc >= 1 && ntn % p.down_nc == 0) return p.down_nc;
     const int64_t tiles = (p.A + BM - 1) / BM + (p.T + BM - 1) / BM;
     return (ntn % 2 == 0 && tiles * (ntn / 2) >= 2 * 512) ? 2 : 1;
 }
@@ -800,7 +796,7 @@ static hipError_t launch_bm(const Plan &p, const uint16_t *x, const moe_weights 
 
     GateUpArgs g;
     g.x = x; g.perm = r.perm;
-    g.T = p.T; g.d = p.d; g.k = p.k; g.G = p.G; g.F = p.F; g.Fs = p.Fs;
+    g.T = p.T; g.d = p.d; g.E = p.E; g.k = p.k; g.G = p.G; g.F = p.F; g.Fs = p.Fs;
     g.gate = w.gate; g.up = w.up; g.sgate = w.sgate; g.sup = w.sup;
     g.tiles = tiles;
     g.ntn_r = (p.F + 127) / 128;
@@ -812,7 +808,7 @@ static hipError_t launch_bm(const Plan &p, const uint16_t *x, const moe_weights 
 
     DownArgs dn;
     dn.h_r = h_r; dn.h_s = h_s; dn.perm = r.perm; dn.topk_w = r.topk_w;
-    dn.T = p.T; dn.d = p.d; dn.k = p.k; dn.G = p.G; dn.F = p.F; dn.Fs = p.Fs;
+    dn.T = p.T; dn.d = p.d; dn.E = p.E; dn.k = p.k; dn.G = p.G; dn.F = p.F; dn.Fs = p.Fs;
     dn.down = w.down; dn.sdown = w.sdown;
     dn.tiles = tiles;
     dn.ntn = (p.d + 255) / 256;

@@ -18,7 +18,7 @@ struct GemmTiles {
 struct GateUpArgs {
     const uint16_t *x;      // [T][d]
     const int32_t *perm;    // [T*k]
-    int T, d, k, G, F, Fs;
+    int T, d, E, k, G, F, Fs;
     moe_qmat gate, up, sgate, sup;
     GemmTiles tiles;
     int ntn_r, ntn_s;       // 128-column blocks per tile (routed, shared)
@@ -32,7 +32,7 @@ struct DownArgs {
     const uint16_t *h_r, *h_s;
     const int32_t *perm;
     const float *topk_w;
-    int T, d, k, G, F, Fs;
+    int T, d, E, k, G, F, Fs;
     moe_qmat down, sdown;
     GemmTiles tiles;
     int ntn;                // 256-column blocks (d / 256, rounded up)
@@ -40,6 +40,30 @@ struct DownArgs {
     int nblk_s, nblk_pad;   // as in GateUpArgs
     uint16_t *obuf;         // [T*k + T][d] weighted outputs: sorted routed rows, then shared
 };
+
+// One routed tile of the block map, read from the caller's routing arrays
+// and clamped into range: expert < E, first row < A = T k, 1 <= rows <=
+// min(tile height, A - first row).  moe_route writes values in range; the
+// clamps keep a corrupt routing input from sending a load outside the
+// caller's arrays.
+struct TileInfo {
+    int e, row0, rows;
+};
+
+__device__ __forceinline__ TileInfo read_tile(const GemmTiles &t, int tile, int E, int A, int BM)
+{
+    TileInfo ti;
+    ti.e = (int)min((uint32_t)t.tile_expert[tile], (uint32_t)(E - 1));
+    ti.row0 = (int)min((uint32_t)t.tile_row0[tile], (uint32_t)(A - 1));
+    ti.rows = max(1, min(t.tile_rows[tile], min(BM, A - ti.row0)));
+    return ti;
+}
+
+// a sorted row's assignment index from perm, clamped to [0, A)
+__device__ __forceinline__ int perm_at(const int32_t *perm, int p, int A)
+{
+    return (int)min((uint32_t)perm[p], (uint32_t)(A - 1));
+}
 
 // Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
 // b % 8).  The grid is sized for the largest possible tile count, while the

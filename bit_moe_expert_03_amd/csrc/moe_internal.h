@@ -21,6 +21,7 @@ constexpr int kMaxDecodeAssign = 512;
 // Everything derived from moe_dims that the launchers need.
 struct Plan {
     int T, d, E, k, F, Fs, G, tile_m;
+    int down_nc;        // requested down-GEMM chain length (0: library picks)
     int64_t A;          // assignments T*k
     int route_tb;       // tokens per route block
     int route_nb;       // route blocks

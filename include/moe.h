@@ -56,8 +56,9 @@ extern "C" {
 #endif
 
 /* 1: route / ffn / layer; 2: optional gated shared expert (moe_weights.shared_gate);
- * 3: moe_router_pack / moe_route_x / moe_router_packed_bytes. */
-#define MOE_ABI_VERSION 3
+ * 3: moe_router_pack / moe_route_x / moe_router_packed_bytes;
+ * 4: moe_dims.down_nc (explicit schedule field, no environment variable). */
+#define MOE_ABI_VERSION 4
 
 #if defined(__GNUC__) || defined(__clang__)
 #define MOE_API __attribute__((visibility("default")))
@@ -76,10 +77,18 @@ typedef enum {
 /* Layer shape.  Supported: 0 <= T <= 2^22 (T*k < 2^31); 1 <= k <= E <= 256;
  * G in {32, 64, 128}; d, F and Fs positive multiples of 64 and of G, at most
  * 16384; T*d, T*k*F and T*Fs below 2^31 (each activation matrix of the
- * prefill path under 4 GiB, addressed with 32-bit offsets).  tile_m: height of a block-map tile, one of {32, 64, 128}, or 0 to
- * let the library pick from T*k/E (moe_tile_m reports the choice). */
+ * prefill path under 4 GiB, addressed with 32-bit offsets).
+ * tile_m: height of a block-map tile, one of {32, 64, 128}, or 0 to let the
+ * library pick from T*k/E (moe_tile_m reports the choice).
+ * down_nc: schedule of the prefill down GEMM, 0 to let the library pick, or
+ * the number of consecutive 256-column blocks of a tile one workgroup runs as
+ * one pipeline: 1, or a divisor of d/256 when d is a multiple of 256 and
+ * F = Fs = 64 * 2^n (n >= 1); other values are MOE_ERR_SHAPE.  It changes the
+ * schedule only, never the result (bit-identical y for every value); the
+ * decode path ignores it. */
 typedef struct {
     int32_t T, d, E, k, F, Fs, G, tile_m;
+    int32_t down_nc;
 } moe_dims;
 
 /* One packed matrix (see the layout above). */
@@ -180,11 +189,10 @@ MOE_API moe_status moe_route_x(const moe_dims *dims, const uint16_t *x, const ui
  * failed" of "Perplexity's Lily Beats MLX-LM by 1.35x Running Qwen3.6 on Apple
  * Silicon"), matrix-vector kernels that stream each token's expert rows.
  * `w` and `r` are host pointers to structs of device pointers; ws must not
- * be shared with a concurrently running call.  Tuning override, read at each
- * call: the environment variable MOE_DOWN_NC (a divisor of d / 256) sets how
- * many 256-column blocks of a tile one down-GEMM workgroup runs as one
- * pipeline, where d is a multiple of 256 and F = Fs = 64 * 2^n; it changes
- * the schedule only, never the result. */
+ * be shared with a concurrently running call.  The routing arrays are read as
+ * moe_route writes them; an out-of-range expert id, tile entry or perm value
+ * is clamped into range (a corrupt routing gives wrong y, never an access
+ * outside the caller's arrays). */
 MOE_API moe_status moe_ffn(const moe_dims *dims, const uint16_t *x, const moe_weights *w,
                    const moe_routing *r, uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 

@@ -61,7 +61,7 @@ def _declare(lib):
     lib.oracle_block_map.argtypes = [ctypes.c_int, _I32P, _I32P, ctypes.c_int, ctypes.c_int, _I32P, _I32P, _I32P]
     lib.oracle_block_map.restype = ctypes.c_int
     lib.oracle_ffn.argtypes = [ctypes.c_int] * 7 + [_U16P, ctypes.POINTER(_OWeights), _U16P, _I32P, _F64P,
-                                                    _I32P, ctypes.c_int, ctypes.c_int, _F64P]
+                                                    _I32P, ctypes.c_int, _F64P]
     lib.oracle_router_logits.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _U16P, _F32P, _F32P, _F64P]
     return lib
 
@@ -172,7 +172,7 @@ def router_logits(x_bits: np.ndarray, w_router: np.ndarray, bias: Optional[np.nd
 
 
 def ffn(dims, x_bits: np.ndarray, weights: dict, ids: np.ndarray, w: np.ndarray,
-        tokens: Optional[Sequence[int]] = None, mirror: bool = False, shared_gate=None,
+        tokens: Optional[Sequence[int]] = None, shared_gate=None,
         lib=None) -> np.ndarray:
     """y (fp64) for all tokens, or for the listed token indices: [len, d].
     shared_gate: optional bf16 bits [d]; the shared expert's output is then
@@ -204,5 +204,5 @@ def ffn(dims, x_bits: np.ndarray, weights: dict, ids: np.ndarray, w: np.ndarray,
         keep.append(sg)
         sg_p = _p(sg, _U16P)
     lib.oracle_ffn(dims.T, dims.d, dims.E, dims.k, dims.F, dims.Fs, dims.G, _p(x_bits, _U16P),
-                   ctypes.byref(W), sg_p, _p(ids, _I32P), _p(w, _F64P), tok_p, ntok, int(mirror), _p(y, _F64P))
+                   ctypes.byref(W), sg_p, _p(ids, _I32P), _p(w, _F64P), tok_p, ntok, _p(y, _F64P))
     return y

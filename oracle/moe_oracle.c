@@ -42,10 +42,8 @@
  * Precision: the exact weight s*q + b is formed in fp64 (s*q has at most 12
  * significant bits, so the sum is exact whenever the two terms are within
  * 2^40 of each other, which holds for every workload here).  The bf16 form
- * that a matrix-core kernel multiplies is defined as bf16_rne(fp32_rne(w)).
- * With mirror != 0 the FFN also rounds w and the SwiGLU output h to bf16,
- * which mimics a bf16 matrix-core pipeline; it is a diagnostic, not the
- * reference result.
+ * that a matrix-core kernel multiplies is defined as bf16_rne(fp32_rne(w));
+ * the FFN itself uses the exact w and keeps h in fp64.
  */
 #include <math.h>
 #include <stdint.h>
@@ -81,11 +79,6 @@ static uint16_t bf16_rne(float f)
     memcpy(&u, &f, 4);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
-}
-
-static double round_to_bf16(double v)
-{
-    return bf16_value(bf16_rne((float)v));
 }
 
 /* 4-bit code of element (n, i) of a [rows][cols] matrix */
@@ -202,24 +195,21 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 /* one SwiGLU expert on one token: out[d] = W_down (silu(W_gate x) * W_up x).
  * gate/up are [Fw][d], down is [d][Fw]; h is scratch of Fw doubles. */
 static void expert_ffn(const omat *gate, const omat *up, const omat *down, int d, int Fw, int G,
-                       const double *x, double *h, double *out, int mirror)
+                       const double *x, double *h, double *out)
 {
     for (int n = 0; n < Fw; ++n) {
         double g = 0.0, u = 0.0;
         for (int i = 0; i < d; ++i) {
             double wg = weight_at(gate, d, G, n, i), wu = weight_at(up, d, G, n, i);
-            if (mirror) { wg = round_to_bf16(wg); wu = round_to_bf16(wu); }
             g += wg * x[i];
             u += wu * x[i];
         }
         h[n] = silu(g) * u;
-        if (mirror) h[n] = round_to_bf16(h[n]);
     }
     for (int i = 0; i < d; ++i) {
         double o = 0.0;
         for (int n = 0; n < Fw; ++n) {
             double wd = weight_at(down, Fw, G, i, n);
-            if (mirror) wd = round_to_bf16(wd);
             o += wd * h[n];
         }
         out[i] = o;
@@ -250,7 +240,7 @@ static double shared_weight(const double *x, const uint16_t *g, int d)
  * fp64, gamma_t = shared_weight(x_t, shared_gate). */
 void oracle_ffn(int T, int d, int E, int k, int F, int Fs, int G, const uint16_t *x,
                 const oweights *W, const uint16_t *shared_gate, const int32_t *ids, const double *w,
-                const int32_t *tokens, int ntok, int mirror, double *y)
+                const int32_t *tokens, int ntok, double *y)
 {
     (void)E;
     int n_out = tokens ? ntok : T;
@@ -269,10 +259,10 @@ void oracle_ffn(int T, int d, int E, int k, int F, int Fs, int G, const uint16_t
             omat g = expert_slab(&W->gate, e, F, d, G);
             omat u = expert_slab(&W->up, e, F, d, G);
             omat dn = expert_slab(&W->down, e, d, F, G);
-            expert_ffn(&g, &u, &dn, d, F, G, xt, h, o, mirror);
+            expert_ffn(&g, &u, &dn, d, F, G, xt, h, o);
             for (int i = 0; i < d; ++i) yt[i] += w[(size_t)t * k + j] * o[i];
         }
-        expert_ffn(&W->sgate, &W->sup, &W->sdown, d, Fs, G, xt, h, o, mirror);
+        expert_ffn(&W->sgate, &W->sup, &W->sdown, d, Fs, G, xt, h, o);
         const double gamma = shared_weight(xt, shared_gate, d);
         for (int i = 0; i < d; ++i) yt[i] += gamma * o[i];
         free(xt);

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = B.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert B.moe_abi_version() == 3
+    assert B.moe_abi_version() == 4
 
 
 def test_status_strings():
@@ -48,6 +48,16 @@ def test_sizes_of_the_workloads(name):
     assert ws >= A * dm.F * 2 + dm.T * dm.Fs * 2 + A * dm.d * 2
 
 
+def test_valid_down_nc_is_accepted():
+    """Every chain length that divides d/256 on a chainable shape is a valid
+    schedule field; 0 and 1 are valid on every shape."""
+    chain = wl.Dims(T=16, d=1024, E=16, k=2, F=128, Fs=128, G=32)
+    for nc in (0, 1, 2, 4):
+        assert B.moe_workspace_bytes(B.make_dims(chain, down_nc=nc)) > 0
+    for nc in (0, 1):
+        assert B.moe_workspace_bytes(B.make_dims(wl.CONFIGS["c0_tiny"], down_nc=nc)) > 0
+
+
 def test_explicit_tile_m_is_kept():
     for tm in (32, 64, 128):
         dm = B.make_dims(wl.CONFIGS["c2_prefill512"], tile_m=tm)
@@ -57,6 +67,9 @@ def test_explicit_tile_m_is_kept():
 BAD = [
     dict(E=0), dict(E=257), dict(k=0), dict(k=17), dict(G=16), dict(d=96), dict(F=100),
     dict(Fs=0), dict(T=-1), dict(tile_m=48), dict(d=64 * 300),
+    # down-GEMM chain lengths that do not fit the shape (d = 256: one column block)
+    dict(down_nc=-1), dict(down_nc=65), dict(down_nc=2), dict(d=512, down_nc=4),
+    dict(d=512, F=192, Fs=192, G=64, down_nc=2), dict(d=512, Fs=256, down_nc=2),
     # activation matrices of 2^31 elements or more (32-bit byte offsets)
     dict(T=1 << 20, d=2048), dict(T=1 << 20, k=8, F=256), dict(T=1 << 20, Fs=2048),
 ]
@@ -64,7 +77,7 @@ BAD = [
 
 @pytest.mark.parametrize("bad", BAD, ids=[str(b) for b in BAD])
 def test_invalid_dims_are_rejected_without_launch(bad):
-    base = dict(T=16, d=256, E=16, k=2, F=128, Fs=128, G=32, tile_m=0)
+    base = dict(T=16, d=256, E=16, k=2, F=128, Fs=128, G=32, tile_m=0, down_nc=0)
     base.update(bad)
     dm = B.moe_dims(**base)
     assert B.moe_tile_m(dm) == 0 and B.moe_max_tiles(dm) == 0 and B.moe_workspace_bytes(dm) == 0

@@ -11,7 +11,7 @@ import torch
 import oracle
 from bit_moe_expert_03_amd import binding as B
 from bit_moe_expert_03_amd import workload as wl
-from gpu_util import (bf16_to_f64, check_routing, check_y, dev, host_u16, run, sample_tokens,
+from gpu_util import (bf16_to_f64, check_routing, check_y, dev, host_u16, run, tile_tokens,
                       weights_to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -144,28 +144,37 @@ def test_layer_tiny_config_all_tokens():
     for tile_m in (0, 32, 64, 128):
         g = run(c, tile_m=tile_m)
         ref = check_routing(c, g)
-        check_y(c, g, ref)
+        check_y(c, g, ref, label=f"c0_tiny tile_m={tile_m}")
 
 
 @pytest.mark.parametrize("tile_m", [0, 32, 128])
-def test_layer_prefill512_sampled(tile_m):
+def test_layer_prefill512_all_tokens(tile_m):
     c = wl.make_case("c2_prefill512")
     g = run(c, tile_m=tile_m, mode="split" if tile_m == 32 else "layer")
     ref = check_routing(c, g)
-    check_y(c, g, ref, tokens=sample_tokens(c, ref, n_random=48))
+    check_y(c, g, ref, key="c2_prefill512", label=f"c2_prefill512 tile_m={tile_m}")
 
 
-@pytest.mark.parametrize("name", ["c3_prefill4096_zipf", "c4_prefill32768"])
-def test_layer_full_size_sampled(name):
-    c = wl.make_case(name)
+def test_layer_prefill4096_zipf_all_tokens():
+    c = wl.make_case("c3_prefill4096_zipf")
     g = run(c)
     ref = check_routing(c, g)
-    check_y(c, g, ref, tokens=sample_tokens(c, ref))
+    check_y(c, g, ref, key="c3_prefill4096_zipf", label="c3_prefill4096_zipf")
+
+
+def test_layer_prefill32768_every_tile():
+    """T = 32768: y on the tokens that put a row into every routed and every
+    shared tile the GEMM kernels run (first and last row of each tile)."""
+    c = wl.make_case("c4_prefill32768")
+    g = run(c)
+    ref = check_routing(c, g)
+    toks = tile_tokens(c, ref, g["tile_m"])
+    check_y(c, g, ref, tokens=toks, key="c4_prefill32768", label="c4_prefill32768 every tile")
 
 
 # Down GEMM with chained column blocks (one block runs several 256-column
-# blocks of its tile as one pipeline): forced through the MOE_DOWN_NC tuning
-# override on shapes with d a multiple of 256 and F = Fs = 64 * 2^n.
+# blocks of its tile as one pipeline): chosen through moe_dims.down_nc on
+# shapes with d a multiple of 256 and F = Fs = 64 * 2^n.
 CHAINED = {
     "chain_T300_d1024_F128": wl.Dims(T=300, d=1024, E=16, k=4, F=128, Fs=128, G=64),
     "chain_T90_d1024_F256_G32": wl.Dims(T=90, d=1024, E=8, k=2, F=256, Fs=256, G=32),
@@ -175,39 +184,38 @@ CHAINED = {
 
 @pytest.mark.parametrize("nc", [2, 4])
 @pytest.mark.parametrize("name", list(CHAINED))
-def test_down_chained_column_blocks(name, nc, monkeypatch):
+def test_down_chained_column_blocks(name, nc):
     dims = CHAINED[name]
     if (dims.d // 256) % nc:
         pytest.skip("chain length must divide the column-block count")
-    monkeypatch.setenv("MOE_DOWN_NC", str(nc))
     c = wl.make_case(dims, seed=200 + list(CHAINED).index(name))
     for tile_m in (0, 32, 128):
-        g = run(c, tile_m=tile_m)
+        g = run(c, tile_m=tile_m, down_nc=nc)
         ref = check_routing(c, g)
         check_y(c, g, ref)
 
 
-def test_down_chain_length_does_not_change_bits(monkeypatch):
+def test_down_chain_length_does_not_change_bits():
     """The chain length changes the schedule only: each output element sees
     the same MFMA sequence, so y is bit-identical for every length."""
     dims = CHAINED["chain_T300_d1024_F128"]
     c = wl.make_case(dims, seed=210)
-    ys = {}
-    for nc in (1, 2, 4):
-        monkeypatch.setenv("MOE_DOWN_NC", str(nc))
-        ys[nc] = run(c)["y_bits"]
+    ys = {nc: run(c, down_nc=nc)["y_bits"] for nc in (1, 2, 4)}
     np.testing.assert_array_equal(ys[1], ys[2])
     np.testing.assert_array_equal(ys[1], ys[4])
 
 
 @pytest.mark.parametrize("nc", [1, 2, 8])
-def test_down_chain_lengths_full_size(nc, monkeypatch):
-    """T = 4096 Zipf at every chain length (the default picks one)."""
-    monkeypatch.setenv("MOE_DOWN_NC", str(nc))
+def test_down_chain_lengths_full_size(nc):
+    """T = 4096 Zipf at every chain length (the default picks one): y on
+    every token that has a row in some tile, and bit-identical to the
+    default schedule."""
     c = wl.make_case("c3_prefill4096_zipf")
-    g = run(c)
+    g = run(c, down_nc=nc)
     ref = check_routing(c, g)
-    check_y(c, g, ref, tokens=sample_tokens(c, ref, n_random=16, seed=nc))
+    check_y(c, g, ref, tokens=tile_tokens(c, ref, g["tile_m"]), key="c3_prefill4096_zipf",
+            label=f"c3_prefill4096_zipf down_nc={nc}")
+    np.testing.assert_array_equal(g["y_bits"], run(c)["y_bits"])
 
 
 GATED = ["ragged_T37_E16_k4", "T300_E16_k4_G64", "T70_E8_k3_G128", "T1_small_decode", "T5_small_batch",
@@ -238,13 +246,13 @@ def test_decode_gated_shared_expert_full_size():
         check_y(c, g, ref)
 
 
-def test_prefill_gated_shared_expert_sampled():
+def test_prefill_gated_shared_expert_all_tokens():
     c = dict(wl.make_case("c2_prefill512"))
     rng = np.random.default_rng(9)
     c["shared_gate"] = wl.to_bf16_bits((rng.standard_normal(c["dims"].d) / np.sqrt(c["dims"].d)).astype(np.float32))
     g = run(c)
     ref = check_routing(c, g)
-    check_y(c, g, ref, tokens=sample_tokens(c, ref, n_random=32))
+    check_y(c, g, ref, label="c2_prefill512 gated shared expert")
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -293,13 +301,13 @@ def test_small_batch_tie_heavy_logits(seed):
         check_y(c, g, ref)
 
 
-@pytest.mark.parametrize("index", [0, 1])
+@pytest.mark.parametrize("index", [0, 1, 39])
 def test_decode_full_size(index):
     c = wl.make_case("c1_decode", index=index)
     for mode in ("layer", "split"):
         g = run(c, mode=mode)
         ref = check_routing(c, g)
-        check_y(c, g, ref)
+        check_y(c, g, ref, label=f"c1_decode set {index} {mode}")
 
 
 # ------------------------------------------------------------------ properties
