@@ -196,9 +196,15 @@ MOE_API moe_status moe_route_x(const moe_dims *dims, const uint16_t *x, const ui
 MOE_API moe_status moe_ffn(const moe_dims *dims, const uint16_t *x, const moe_weights *w,
                    const moe_routing *r, uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 
-/* moe_route followed by moe_ffn.  For small batches (1 <= T <= 8 and
- * T*k <= 512) the routing is computed inside the matrix-vector kernels (every
- * field of *out is still written, identical to moe_route's). */
+/* The whole layer: moe_route followed by moe_ffn, enqueued as one sequence
+ * on `stream` with no host round trip between the routing and the experts
+ * (page "Perplexity's Lily Beats MLX-LM by 1.35x Running Qwen3.6 on Apple
+ * Silicon", section "Prefill optimizations", second bullet: the routing
+ * metadata is built on the GPU inside the same submission as the expert
+ * matrices; section "What Lily actually does": k routed experts plus the
+ * shared expert per token).  For small batches (1 <= T <= 8 and T*k <= 512)
+ * the routing is computed inside the matrix-vector kernels (every field of
+ * *out is still written, identical to moe_route's). */
 MOE_API moe_status moe_layer(const moe_dims *dims, const float *logits, const uint16_t *x,
                      const moe_weights *w, const moe_routing *out, uint16_t *y,
                      void *ws, size_t ws_bytes, void *stream);
@@ -222,9 +228,16 @@ MOE_API moe_status moe_layer_timed(const moe_dims *dims, const float *logits, co
                                    int32_t n_events);
 
 /* Decode a packed [rows][cols] matrix to bf16 [rows][cols] with the same
- * device routine the GEMM kernels use: bf16_rne(fp32_rne(s*q + b)).  A test
- * and inspection export; the layer itself never materialises this array.
- * Needs cols a multiple of 32 and of G, G in {32, 64, 128}. */
+ * device routine the GEMM kernels use: bf16_rne(fp32_rne(s*q + b)), the
+ * groupwise affine 4-bit format (page "Perplexity Open Sources Lily: Rust &
+ * Metal Engine for Qwen3.6", paragraph on the model) expanded to the bf16
+ * values the matrix kernels multiply (page "Perplexity's Lily Beats MLX-LM by
+ * 1.35x Running Qwen3.6 on Apple Silicon", section "Prefill optimizations",
+ * first bullet: tiles are unpacked on chip right before the multiply).  A
+ * test and inspection export; the layer itself never materialises this
+ * array.  Needs cols a multiple of 32 and of G, G in {32, 64, 128}; out_bf16
+ * is caller-owned, rows*cols bf16; invalid arguments return a status with
+ * nothing enqueued. */
 MOE_API moe_status moe_dequant(const moe_qmat *m, int32_t rows, int32_t cols, int32_t G,
                        uint16_t *out_bf16, void *stream);
 
