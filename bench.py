@@ -11,8 +11,11 @@ distinct layer weight sets (455 MB each, 18.2 GB in all) so that weights
 stream from HBM and not from cache; each step has its own x and logits.  The
 K timed steps are one HIP graph of K layer calls.
 
-Second object (`prefill`): T = 4096 tokens with Zipf-skewed routing, one
-weight set, timed the same way.
+Further objects: `prefill` (T = 4096 tokens with Zipf-skewed routing, the
+prefill half of the metric), `prefill512` (T = 512) and `prefill32768`
+(T = 32768), one weight set each, timed the same way.  The decode graph
+visits min(K, 40) weight sets and the caches are flushed before every timed
+replay, so the weights always come from HBM.
 
 Per-kernel durations come from HIP start/stop events of each dispatch
 (moe_layer_timed launches every kernel through hipExtLaunchKernel with an
@@ -156,15 +159,29 @@ def layer_flops(dims):
     return dims.T * (dims.k * 6 * dims.d * dims.F + 6 * dims.d * dims.Fs)
 
 
-def run_timed(B, dm, calls, steps, warmup):
+class CacheFlush:
+    """Evicts the 256 MB Infinity Cache and the L2s between timed replays
+    (outside the timed region): a device copy of 1 GiB."""
+
+    def __init__(self):
+        import torch
+        self.src = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+        self.dst = torch.empty_like(self.src)
+
+    def __call__(self):
+        self.dst.copy_(self.src)
+
+
+def run_timed(B, dm, calls, steps, warmup, flush=None):
     """calls[i] = (logits, x, weights_struct, y) for step i % len(calls).
 
     Timed region: one HIP graph of `steps` consecutive layer calls, replayed
-    once untimed (upload) and once timed between device synchronisations.
-    Per-kernel times: right after, the same `steps` calls eagerly through
-    moe_layer_timed, whose kernels are launched with start/stop events
-    (hipExtLaunchKernel) on the launch stream.  Returns (seconds, mean ms per
-    kernel)."""
+    once untimed (upload) and three times timed between device
+    synchronisations (median); with `flush`, the caches are flushed before
+    each replay, outside the timed region.  Per-kernel times: right after,
+    the same `steps` calls eagerly through moe_layer_timed, whose kernels are
+    launched with start/stop events (hipExtLaunchKernel) on the launch
+    stream.  Returns (seconds, mean ms per kernel)."""
     import torch
     nk = B.moe_layer_kernels(dm)
     r = B.alloc_routing(dm)
@@ -186,12 +203,18 @@ def run_timed(B, dm, calls, steps, warmup):
     torch.cuda.synchronize()
     reps = []
     for _ in range(3):  # median of three timed replays
+        if flush:
+            flush()
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         g.replay()
         torch.cuda.synchronize()
         reps.append(time.perf_counter() - t0)
     reps.sort()
     evs = [make_events(2 * nk) for _ in range(steps)]
+    if flush:
+        flush()
+    torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for i in range(steps):
             lg, x, w, y = calls[i % len(calls)]
@@ -225,24 +248,33 @@ def bench_decode(B, wl, args):
         calls.append((to_dev(c["logits"]), to_dev(c["x"]), sets[s][1], y))
         host_inputs.append(c)
     log("decode: capturing and timing")
-    sec, per_kernel = run_timed(B, dm, calls, args.steps, args.warmup)
+    flush = CacheFlush()
+    sec, per_kernel = run_timed(B, dm, calls, args.steps, args.warmup, flush)
     value = args.steps / sec
-    gu_ms = per_kernel[0]
-    gu_bytes = gateup_decode_bytes(dims)
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    if len(per_kernel) == 1:  # one-launch decode: the kernel is the whole layer
+        names, kernel = ["decode_fused"], "decode_fused_kernel"
+        dom_bytes = decode_layer_bytes(dims) + dims.E * 4
+    else:
+        names, kernel = ["decode_gateup", "decode_down"], "decode_gateup_kernel"
+        dom_bytes = gateup_decode_bytes(dims)
+    dom_ms = per_kernel[0]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     out = {
         "value": value,
         "ms_per_step": sec * 1e3 / args.steps,
-        "per_kernel_ms": {"decode_gateup": per_kernel[0], "decode_down": per_kernel[1]},
+        "per_kernel_ms": dict(zip(names, per_kernel)),
         "layer_bytes": decode_layer_bytes(dims),
         "layer_gbs": decode_layer_bytes(dims) / (sec / args.steps) / 1e9,
-        "roofline": {"bound": "hbm", "kernel": "decode_gateup_kernel", "achieved": achieved,
+        "weight_sets_touched_per_replay": min(args.steps, nsets),
+        "bytes_touched_per_replay": min(args.steps, nsets) * decode_layer_bytes(dims),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("decode_gateup_kernel"), "bytes_per_launch": gu_bytes,
-                     "avg_launch_ms": gu_ms},
+                     "traffic": measured_traffic(kernel), "bytes_per_launch": dom_bytes,
+                     "avg_launch_ms": dom_ms},
     }
-    log(f"decode: {value:.0f} tok/s, {out['ms_per_step'] * 1e3:.2f} us/step, gate/up {gu_ms * 1e3:.2f} us "
-        f"({achieved:.0f} GB/s), down {per_kernel[1] * 1e3:.2f} us")
+    log(f"decode: {value:.0f} tok/s, {out['ms_per_step'] * 1e3:.2f} us/step, "
+        + ", ".join(f"{n} {t * 1e3:.2f} us" for n, t in zip(names, per_kernel)) + f" ({achieved:.0f} GB/s)")
+    del flush
     out["small_batches"] = None if args.no_small_batches else bench_small_batches(B, wl, args, dims, seed, sets)
     del sets, calls
     torch.cuda.empty_cache()
@@ -271,40 +303,53 @@ def bench_small_batches(B, wl, args, dims, seed, sets):
     return out
 
 
-def bench_prefill(B, wl, args):
+PREFILL_WORKLOADS = {
+    # key in the JSON line: (workload name, description)
+    "prefill": ("c3_prefill4096_zipf", "prefill T=4096 Zipf(1)-skewed routing"),
+    "prefill512": ("c2_prefill512", "prefill T=512 near-uniform routing"),
+    "prefill32768": ("c4_prefill32768", "prefill T=32768 near-uniform routing"),
+}
+
+
+def bench_prefill(B, wl, args, name, desc, steps):
+    """One prefill workload: the whole layer (routing + FFN) from device
+    logits and x to device y, one weight set, `steps` layer calls in a graph;
+    roofline of the gate/up GEMM (useful bf16 MFMA flops per launch)."""
     import torch
-    name = "c3_prefill4096_zipf"
     c = wl.make_case(name)
     dims = c["dims"]
     dm = B.make_dims(dims)
     wd = {m: {f: to_dev(c["w"][m][f]) for f in ("q", "s", "b")} for m in wl.MATS}
     y = torch.empty((dims.T, dims.d), dtype=torch.int16, device="cuda")
     calls = [(to_dev(c["logits"]), to_dev(c["x"]), B.weights_struct(wd), y)]
-    log("prefill: capturing and timing")
-    sec, per_kernel = run_timed(B, dm, calls, args.prefill_steps, 3)
+    log(f"{name}: capturing and timing")
+    sec, per_kernel = run_timed(B, dm, calls, steps, 3)
     names = ["route_topk", "route_scan", "route_scatter", "gateup_gemm", "down_gemm", "combine"]
-    value = dims.T * args.prefill_steps / sec
+    value = dims.T * steps / sec
     gu_ms = per_kernel[3]
     fl = gateup_flops(dims)
     achieved = fl / (gu_ms * 1e-3) / 1e12
-    ms = sec * 1e3 / args.prefill_steps
+    ms = sec * 1e3 / steps
     out = {
-        "value": value, "unit": "tokens/s", "ms_per_step": ms, "steps": args.prefill_steps,
+        "value": value, "unit": "tokens/s", "ms_per_step": ms, "steps": steps,
         "dtype": "bf16",
-        "config": {"workload": "prefill T=4096 Zipf(1)-skewed routing, d=2048, E=256, top-8 + shared, "
-                               "F=Fs=512, int4 G=64, one weight set", "T": dims.T},
+        "config": {"workload": f"{desc}, d=2048, E=256, top-8 + shared, F=Fs=512, int4 G=64, one weight set",
+                   "T": dims.T},
         "per_kernel_ms": dict(zip(names, per_kernel)),
         "routing_gbs": (dims.T * dims.E * 4 + dims.T * dims.k * 16) / (sum(per_kernel[:3]) * 1e-3) / 1e9,
         "layer_tflops": layer_flops(dims) / (ms * 1e-3) / 1e12,
         "layer_mfma_frac": layer_flops(dims) / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
         "roofline": {"bound": "mfma", "kernel": "moe_gateup_kernel", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFS,
-                     "traffic": measured_traffic("moe_gateup_kernel"), "flops_per_launch": fl,
-                     "avg_launch_ms": gu_ms},
+                     "traffic": measured_traffic("moe_gateup_kernel") if name == "c3_prefill4096_zipf" else None,
+                     "flops_per_launch": fl, "avg_launch_ms": gu_ms},
     }
-    log(f"prefill: {value / 1e6:.2f} M tok/s, {ms * 1e3:.1f} us/step, kernels "
+    log(f"{name}: {value / 1e6:.2f} M tok/s, {ms * 1e3:.1f} us/step, kernels "
         + ", ".join(f"{n} {t * 1e3:.1f}us" for n, t in zip(names, per_kernel)))
-    out["route_from_x"] = bench_route_x(B, wl, c, dm)
+    if name == "c3_prefill4096_zipf":
+        out["route_from_x"] = bench_route_x(B, wl, c, dm)
+    del wd, calls, y
+    torch.cuda.empty_cache()
     return out, c
 
 
@@ -340,21 +385,29 @@ def bench_route_x(B, wl, c, dm, reps=20):
 
 
 def cpu_baseline_decode(wl, host, seconds):
+    """The oracle on decode tokens: each call routes and runs the fp64 FFN of
+    a batch of independent T = 1 decode steps that share one weight set, so
+    the oracle's OpenMP loop over tokens uses every host core."""
+    import numpy as np
     import oracle
     dims, host_sets, host_inputs = host
+    nb = max(1, oracle.threads())
     t0 = time.perf_counter()
-    n = 0
+    n, calls = 0, 0
     while True:
-        c = host_inputs[n % len(host_inputs)]
-        r = oracle.route(c["logits"], dims.k, 32)
-        oracle.ffn(dims, c["x"], host_sets[n % len(host_sets)], r["ids"], r["w"])
-        n += 1
+        cs = [host_inputs[(n + i) % len(host_inputs)] for i in range(nb)]
+        x = np.concatenate([c["x"] for c in cs])
+        lg = np.concatenate([c["logits"] for c in cs])
+        r = oracle.route(lg, dims.k, 32)
+        oracle.ffn(dims.replace(T=nb), x, host_sets[calls % len(host_sets)], r["ids"], r["w"])
+        n += nb
+        calls += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle", "host": host_cpu(),
-            "sample": f"{n} decode steps (T=1, route + fp64 FFN), 2 weight sets held in host memory; "
-                      "one token per call, so the oracle's token loop runs on one thread"}
+    return {"value": n / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle", "host": host_cpu(),
+            "sample": f"{n} decode tokens (T=1 steps: route + fp64 FFN), {nb} independent steps per oracle call "
+                      f"sharing one of {len(host_sets)} weight sets, OpenMP over the steps"}
 
 
 def cpu_baseline_prefill(wl, c, seconds):
@@ -372,7 +425,7 @@ def cpu_baseline_prefill(wl, c, seconds):
             break
     return {"value": ntok / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle", "host": host_cpu(),
             "sample": f"routing of all {dims.T} tokens + fp64 FFN of the first {ntok} tokens of the "
-                      "T=4096 Zipf workload (OpenMP over tokens)"}
+                      f"T={dims.T} workload (OpenMP over tokens)"}
 
 
 def main():
@@ -407,16 +460,20 @@ def main():
     log(f"achievable: copy {peaks['hbm_copy_gbs']:.0f} GB/s, bf16 matmul {peaks['bf16_matmul_tflops']:.0f} TFLOP/s")
     dec, host = bench_decode(B, wl, args)
     dec["roofline"]["frac_of_achievable"] = dec["roofline"]["achieved"] / peaks["hbm_copy_gbs"]
-    pre = c3 = None
+    pre = {}
     if not args.no_prefill:
-        pre, c3 = bench_prefill(B, wl, args)
-        pre["roofline"]["frac_of_achievable"] = pre["roofline"]["achieved"] / peaks["bf16_matmul_tflops"]
+        for key, (name, desc) in PREFILL_WORKLOADS.items():
+            steps = args.prefill_steps if name != "c4_prefill32768" else max(3, args.prefill_steps // 4)
+            out, case = bench_prefill(B, wl, args, name, desc, steps)
+            out["roofline"]["frac_of_achievable"] = out["roofline"]["achieved"] / peaks["bf16_matmul_tflops"]
+            if not args.no_cpu_baseline:
+                out["cpu_baseline"] = cpu_baseline_prefill(wl, case, args.cpu_seconds)
+            pre[key] = out
+            del case
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline_decode(wl, host, args.cpu_seconds)
-        if pre is not None:
-            pre["cpu_baseline"] = cpu_baseline_prefill(wl, c3, args.cpu_seconds)
     line = {
         "metric": METRIC,
         "value": dec["value"],
@@ -428,14 +485,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
+        "dtype_detail": "int4 groupwise-affine weights, bf16 activations and products, fp32 accumulation",
         "data": "synthetic",
         "config": {"workload": "decode T=1, d=2048, E=256, top-8 + shared, F=Fs=512, int4 G=64, "
-                               "40 layer weight sets rotated per step", "T": 1, "weight_sets": 40},
+                               "40 layer weight sets rotated per step, caches flushed before each timed replay",
+                   "T": 1, "weight_sets": 40, "weight_sets_touched_per_replay": min(args.steps, 40)},
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
         "decode_detail": {k: dec[k] for k in ("per_kernel_ms", "layer_bytes", "layer_gbs", "small_batches")},
-        "prefill": pre,
+        "prefill": pre.get("prefill"),
+        "prefill512": pre.get("prefill512"),
+        "prefill32768": pre.get("prefill32768"),
         "achievable": peaks,
     }
     print(json.dumps(line), flush=True)

@@ -266,8 +266,12 @@ MOE_API moe_status moe_ffn(const moe_dims *dims, const uint16_t *x, const moe_we
     if ((st = check_weights(p, w)) || (st = check_routing(p, r))) return st;
     if (p.T == 0) return MOE_OK;
     (void)hipGetLastError();
-    hipError_t e = decode_batch(p) ? launch_decode(p, nullptr, x, *w, *r, y, ws, (hipStream_t)stream)
-                                   : launch_ffn_gemm(p, x, *w, *r, y, ws, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (decode_batch(p))
+        e = launch_decode(p, nullptr, x, *w, *r, y, ws, s);
+    else
+        e = launch_ffn_gemm(p, x, *w, *r, y, ws, s);
     return hip_status(e, "moe_ffn launch");
 }
 

@@ -18,6 +18,7 @@ constexpr int kMaxE = 256;
 constexpr int kMaxDecodeT = 8;
 constexpr int kMaxDecodeAssign = 512;
 
+
 // Everything derived from moe_dims that the launchers need.
 struct Plan {
     int T, d, E, k, F, Fs, G, tile_m;
@@ -78,8 +79,9 @@ hipError_t launch_ffn_gemm(const Plan &p, const uint16_t *x, const moe_weights &
                            const moe_routing &r, uint16_t *y, void *ws, hipStream_t s,
                            EventTrace *tr = nullptr);
 
-// ---- decode.hip (T == 1 path); when logits != nullptr the routing is
-// computed in-kernel and written to r, else it is read from r.
+// ---- decode.hip (batches of 1..kMaxDecodeT tokens, two kernels); when
+// logits != nullptr the routing is computed in-kernel and written to r,
+// else it is read from r.
 hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
                          const moe_weights &w, const moe_routing &r, uint16_t *y, void *ws,
                          hipStream_t s, EventTrace *tr = nullptr);

@@ -126,12 +126,13 @@ def test_null_pointers_and_small_workspace_are_rejected():
     assert L.moe_dequant(ctypes.byref(q), 4, 48, 32, _fake_ptr(63), None) == B.MOE_ERR_SHAPE
 
 
-def test_small_batches_take_the_two_decode_kernels():
+def test_kernel_counts_of_each_path():
     """1 <= T <= 8 with T*k <= 512: two kernels (decode gate/up with routing,
     decode down); larger batches: three routing kernels and three GEMM-path
-    kernels."""
+    kernels; T = 0: one."""
     base = dict(d=256, E=128, F=128, Fs=128, G=64)
-    for T, k, n in [(1, 8, 2), (2, 8, 2), (8, 8, 2), (8, 64, 2), (9, 8, 6), (8, 65, 6), (4096, 8, 6), (0, 8, 1)]:
+    for T, k, n in [(1, 8, 2), (1, 17, 2), (2, 8, 2), (8, 8, 2), (8, 64, 2), (9, 8, 6), (8, 65, 6),
+                    (4096, 8, 6), (0, 8, 1)]:
         dm = B.make_dims(wl.Dims(T=T, k=k, **base))
         assert B.moe_layer_kernels(dm) == n, (T, k)
 
