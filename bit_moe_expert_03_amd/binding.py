@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_ERR_ARG, MOE_ERR_SHAPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 EXPORTS = ("moe_abi_version", "moe_tile_m", "moe_max_tiles", "moe_workspace_bytes", "moe_route",
            "moe_ffn", "moe_layer", "moe_layer_kernels", "moe_layer_timed", "moe_dequant",
-           "moe_router_packed_bytes", "moe_router_pack", "moe_route_x",
+           "moe_router_packed_bytes", "moe_router_pack", "moe_route_x", "moe_layer_noalloc",
            "moe_status_string", "moe_last_error")
 MATS = ("gate", "up", "down", "sgate", "sup", "sdown")
 
@@ -73,13 +73,14 @@ def lib():
         L.moe_route.argtypes = [P(moe_dims), vp, P(moe_routing), vp, sz, vp]
         L.moe_ffn.argtypes = [P(moe_dims), vp, P(moe_weights), P(moe_routing), vp, vp, sz, vp]
         L.moe_layer.argtypes = [P(moe_dims), vp, vp, P(moe_weights), P(moe_routing), vp, vp, sz, vp]
+        L.moe_layer_noalloc.argtypes = [P(moe_dims), vp, vp, P(moe_weights), P(moe_routing), vp, vp]
         L.moe_layer_timed.argtypes = [P(moe_dims), vp, vp, P(moe_weights), P(moe_routing), vp, vp, sz,
                                       vp, P(ctypes.c_void_p), ctypes.c_int32]
         L.moe_dequant.argtypes = [P(moe_qmat), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
         L.moe_router_pack.argtypes = [P(moe_dims), vp, vp, vp]
         L.moe_route_x.argtypes = [P(moe_dims), vp, vp, vp, vp, P(moe_routing), vp, sz, vp]
         for f in ("moe_route", "moe_ffn", "moe_layer", "moe_layer_timed", "moe_dequant", "moe_router_pack",
-                  "moe_route_x"):
+                  "moe_route_x", "moe_layer_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -204,6 +205,18 @@ def moe_layer(dims: moe_dims, logits: torch.Tensor, x: torch.Tensor, weights,
     r = routing_struct(routing)
     _check(lib().moe_layer(ctypes.byref(dims), _ptr(logits), _ptr(x), ctypes.byref(w),
                            ctypes.byref(r), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
+
+
+def moe_layer_noalloc(dims: moe_dims, logits: torch.Tensor, x: torch.Tensor, weights,
+                      routing: Dict[str, torch.Tensor], y: torch.Tensor, stream=None):
+    """moe_layer on the library's own device scratch array (no workspace)."""
+    w = weights if isinstance(weights, moe_weights) else weights_struct(weights)
+    r = routing_struct(routing)
+    _check(lib().moe_layer_noalloc(ctypes.byref(dims), _ptr(logits), _ptr(x), ctypes.byref(w),
+                                   ctypes.byref(r), _ptr(y), _stream(stream)))
 
 
 def moe_layer_kernels(dims: moe_dims) -> int:

@@ -8,6 +8,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
@@ -282,20 +283,23 @@ static int layer_kernels(const Plan &p)
     return 3 + 3;                        // route topk, scan, scatter; gate/up, down, combine
 }
 
-static moe_status layer_impl(const moe_dims *dims, const float *logits, const uint16_t *x,
-                             const moe_weights *w, const moe_routing *out, uint16_t *y, void *ws,
-                             size_t ws_bytes, void *stream, EventTrace *tr)
+// the layer's pointer arguments (everything but the workspace)
+static moe_status check_layer_args(const Plan &p, const float *logits, const uint16_t *x, const moe_weights *w,
+                                   const moe_routing *out, const uint16_t *y)
 {
-    Plan p;
-    moe_status st = common(dims, &p, ws, ws_bytes);
-    if (st) return st;
+    moe_status st;
     const size_t xb = (size_t)p.T * p.d * 2;
     if (!ptr_ok(logits, (size_t)p.T * p.E * 4)) return fail(MOE_ERR_ARG, "logits: null or misaligned pointer");
     if (!ptr_ok(x, xb) || !ptr_ok(y, xb)) return fail(MOE_ERR_ARG, "x / y: null or misaligned pointer");
     if (overlap(x, xb, y, xb)) return fail(MOE_ERR_ARG, "x and y overlap");
     if ((st = check_weights(p, w)) || (st = check_routing(p, out))) return st;
-    if (tr && tr->n < 2 * layer_kernels(p))
-        return fail(MOE_ERR_ARG, "need %d events, got %d", 2 * layer_kernels(p), tr->n);
+    return MOE_OK;
+}
+
+// route + ffn on validated arguments
+static moe_status launch_layer(const Plan &p, const float *logits, const uint16_t *x, const moe_weights *w,
+                               const moe_routing *out, uint16_t *y, void *ws, void *stream, EventTrace *tr)
+{
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     hipError_t e;
@@ -308,11 +312,80 @@ static moe_status layer_impl(const moe_dims *dims, const float *logits, const ui
     return hip_status(e, "moe_layer launch");
 }
 
+static moe_status layer_impl(const moe_dims *dims, const float *logits, const uint16_t *x,
+                             const moe_weights *w, const moe_routing *out, uint16_t *y, void *ws,
+                             size_t ws_bytes, void *stream, EventTrace *tr)
+{
+    Plan p;
+    moe_status st = common(dims, &p, ws, ws_bytes);
+    if (st) return st;
+    if ((st = check_layer_args(p, logits, x, w, out, y))) return st;
+    if (tr && tr->n < 2 * layer_kernels(p))
+        return fail(MOE_ERR_ARG, "need %d events, got %d", 2 * layer_kernels(p), tr->n);
+    return launch_layer(p, logits, x, w, out, y, ws, stream, tr);
+}
+
+// ---- allocation-free entry point ------------------------------------------------
+//
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the workspace is a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES
+// that the code object brings with it (each GPU the library runs on holds its
+// own copy until the process ends).  Its device address is looked up once per
+// device with that device current and kept; the array's name is never used in
+// host code as an address.  No kernel needs any of it to start at zero: every
+// element a kernel reads was written earlier in the same call.
+
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// the current device's copy of `scratch` (nullptr and *why set on failure)
+static void *scratch_address(const char **why)
+{
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *why = "no current HIP device (or device index >= 64)";
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            *why = hipGetErrorString(e);
+            return nullptr;
+        }
+        addr[dev] = ptr;
+    }
+    return addr[dev];
+}
+
 MOE_API moe_status moe_layer(const moe_dims *dims, const float *logits, const uint16_t *x,
                              const moe_weights *w, const moe_routing *out, uint16_t *y, void *ws,
                              size_t ws_bytes, void *stream)
 {
     return layer_impl(dims, logits, x, w, out, y, ws, ws_bytes, stream, nullptr);
+}
+
+MOE_API moe_status moe_layer_noalloc(const moe_dims *dims, const float *logits, const uint16_t *x,
+                                     const moe_weights *w, const moe_routing *out, uint16_t *y, void *stream)
+{
+    Plan p;
+    const char *why = "";
+    moe_status st = make_plan(dims, &p, &why);
+    if (st != MOE_OK) return fail(st, "%s", why);
+    if (p.ws_bytes > MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_WORKSPACE,
+                    "these dims need %zu bytes of workspace; the allocation-free entry point holds %zu "
+                    "(call moe_layer with a caller-owned workspace)",
+                    p.ws_bytes, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    if ((st = check_layer_args(p, logits, x, w, out, y))) return st;
+    void *ws = scratch_address(&why);
+    if (!ws) return fail(MOE_ERR_HIP, "scratch address: %s", why);
+    (void)hipGetLastError();
+    return launch_layer(p, logits, x, w, out, y, ws, stream, nullptr);
 }
 
 MOE_API int32_t moe_layer_kernels(const moe_dims *dims)

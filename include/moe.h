@@ -209,6 +209,26 @@ MOE_API moe_status moe_layer(const moe_dims *dims, const float *logits, const ui
                      const moe_weights *w, const moe_routing *out, uint16_t *y,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of the device scratch array behind moe_layer_noalloc: dims with
+ * moe_workspace_bytes() above this are rejected by it (32 MiB: T = 512 at
+ * d = 2048, E = 256, k = 8, F = Fs = 512 needs about 24 MB). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* moe_layer without a workspace argument, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library's code object (one per GPU,
+ * held until the process ends); the call itself allocates nothing.  The
+ * caller still owns x, y, the weights and every routing array, exactly as in
+ * moe_layer, and gets identical results.  Dims whose moe_workspace_bytes()
+ * exceed MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE with nothing
+ * enqueued.  Every call on one GPU uses that GPU's one array: calls that
+ * overlap on one GPU (different streams, host threads) race and must be
+ * serialised by the caller.  Asynchronous on `stream`. */
+MOE_API moe_status moe_layer_noalloc(const moe_dims *dims, const float *logits, const uint16_t *x,
+                                     const moe_weights *w, const moe_routing *out, uint16_t *y,
+                                     void *stream);
+
 /* Host-only, pure.  Number of kernels one moe_layer call launches for these
  * dims, in launch order: small batches (1 <= T <= 8, T*k <= 512): decode
  * gate/up (with routing), decode down; larger T: route top-k, route scan,

@@ -151,3 +151,29 @@ def test_router_packed_bytes_and_argument_checks():
                          B.moe_workspace_bytes(dm), None) == B.MOE_ERR_ARG
     bad = B.make_dims(wl.CONFIGS["c1_decode"].replace(E=0))
     assert B.moe_router_packed_bytes(bad) == 0
+
+
+def test_noalloc_entry_point_rejects_before_any_device_call():
+    """moe_layer_noalloc: dims whose workspace exceeds its scratch array
+    (T = 4096: about 213 MiB against 32 MiB) and null pointers are refused on
+    the host, before the scratch address is looked up or anything launched."""
+    L = B.lib()
+    big = B.make_dims(wl.CONFIGS["c3_prefill4096_zipf"])
+    assert B.moe_workspace_bytes(big) > B.NOALLOC_SCRATCH_BYTES
+    r = B.moe_routing(*[_fake_ptr(i) for i in range(10)])
+    w = B.moe_weights(*[B.moe_qmat(_fake_ptr(30 + 3 * i), _fake_ptr(31 + 3 * i), _fake_ptr(32 + 3 * i))
+                        for i in range(6)])
+    st = L.moe_layer_noalloc(ctypes.byref(big), _fake_ptr(20), _fake_ptr(50), ctypes.byref(w), ctypes.byref(r),
+                             _fake_ptr(51), None)
+    assert st == B.MOE_ERR_WORKSPACE and L.moe_last_error()
+    small = B.make_dims(wl.CONFIGS["c0_tiny"])
+    assert B.moe_workspace_bytes(small) <= B.NOALLOC_SCRATCH_BYTES
+    st = L.moe_layer_noalloc(ctypes.byref(small), None, _fake_ptr(50), ctypes.byref(w), ctypes.byref(r),
+                             _fake_ptr(51), None)
+    assert st == B.MOE_ERR_ARG
+
+
+def test_noalloc_limit_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
