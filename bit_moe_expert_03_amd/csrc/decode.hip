@@ -160,11 +160,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
     } else {
         int e;
         if (a.logits) {
-            uint32_t key[4];
-            const LogitQuad lq = load_logits(a.logits + (size_t)t * a.E, a.E);
+            // the four waves of a block share the token and the slot (the
+            // waves of a token and of a slot are multiples of four): wave 0
+            // runs the selection rounds and hands the expert over through
+            // LDS.  Rounds run by every wave keep the compute unit's scalar
+            // unit busy and delay all of them (measured).
+            __shared__ int s_expert;
+            if (wave == 0) {
+                uint32_t key[4];
+                const LogitQuad lq = load_logits(a.logits + (size_t)t * a.E, a.E);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) key[c] = (4 * lane + c < a.E) ? logit_key(lq.v[c]) : 0u;
-            e = wave_rank_expert(key, slot);
+                for (int c = 0; c < 4; ++c) key[c] = (4 * lane + c < a.E) ? logit_key(lq.v[c]) : 0u;
+                const int ew = wave_rank_expert(key, slot);
+                if (lane == 0) s_expert = ew;
+            }
+            __syncthreads();
+            e = s_expert;
         } else {
             e = min((uint32_t)a.r.topk_ids[t * a.k + slot], (uint32_t)(a.E - 1));  // ids from the caller: kept in range
         }
@@ -279,6 +290,8 @@ static void launch_gateup(EventTrace *tr, DecodeArgs &a, hipStream_t s)
 {
     a.wps_r = a.F / P;
     a.wps_s = a.Fs / P;
+    // the selection hand-over above needs every block inside one slot of one token
+    static_assert(kDecThreads / kWave == 4 && 64 % (4 * P) == 0, "F / P and Fs / P multiples of the block's 4 waves");
     const int waves = a.T * (a.k * a.wps_r + a.wps_s);
     const int nb = 1 + (waves + kDecThreads / kWave - 1) / (kDecThreads / kWave);
     launch(tr, decode_gateup_kernel<NCH, P>, dim3(nb), dim3(kDecThreads), 0, s, a);
