@@ -162,6 +162,15 @@ def test_layer_prefill4096_zipf_all_tokens():
     check_y(c, g, ref, key="c3_prefill4096_zipf", label="c3_prefill4096_zipf")
 
 
+def test_tile_heights_give_identical_bits_full_size():
+    """T = 4096 Zipf: y at every tile height is bit-identical (the tile
+    height changes which rows share a workgroup, never the order of a sum)."""
+    c = wl.make_case("c3_prefill4096_zipf")
+    ys = {tm: run(c, tile_m=tm)["y_bits"] for tm in (32, 64, 128)}
+    for tm in (32, 64):
+        np.testing.assert_array_equal(ys[tm], ys[128], err_msg=f"tile_m={tm}")
+
+
 def test_layer_prefill32768_every_tile():
     """T = 32768: y on the tokens that put a row into every routed and every
     shared tile the GEMM kernels run (first and last row of each tile)."""
