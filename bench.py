@@ -288,7 +288,7 @@ def bench_small_batches(B, wl, args, dims, seed, sets):
     import torch
     out = {}
     steps = max(8, args.steps // 4)
-    for T in (2, 4, 8):
+    for T in (2, 4, 8, 16, 32):
         dT = dims.replace(T=T)
         dm = B.make_dims(dT)
         calls = []

@@ -14,8 +14,11 @@ namespace moe {
 constexpr int kRouteThreads = 1024;  // routing kernels: 16 waves per block
 constexpr int kMaxE = 256;
 // batches of up to kMaxDecodeT tokens (and at most kMaxDecodeAssign token-
-// expert assignments) take the matrix-vector kernels of the decode path
-constexpr int kMaxDecodeT = 8;
+// expert assignments) take the matrix-vector kernels of the decode path.
+// Measured at d = 2048, E = 256, k = 8, F = Fs = 512 (one weight set, layer
+// time): T = 9: 43 us against 82 us on the GEMM path, T = 16: 71 against 90,
+// T = 24: 101 against 120, T = 32: 130 against 132.
+constexpr int kMaxDecodeT = 32;
 constexpr int kMaxDecodeAssign = 512;
 
 

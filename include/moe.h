@@ -184,7 +184,7 @@ MOE_API moe_status moe_route_x(const moe_dims *dims, const uint16_t *x, const ui
 
 /* Expert FFN: x bf16 [T][d] + weights + routing (as produced by moe_route)
  * -> y bf16 [T][d].  Grouped GEMMs over the block map with the 4-bit weights
- * decoded inside the kernel, or, for small batches (1 <= T <= 8 and T*k <= 512:
+ * decoded inside the kernel, or, for small batches (1 <= T <= 32 and T*k <= 512:
  * single-token decode and the pages' few-token verify passes, section "What
  * failed" of "Perplexity's Lily Beats MLX-LM by 1.35x Running Qwen3.6 on Apple
  * Silicon"), matrix-vector kernels that stream each token's expert rows.
@@ -202,7 +202,7 @@ MOE_API moe_status moe_ffn(const moe_dims *dims, const uint16_t *x, const moe_we
  * Silicon", section "Prefill optimizations", second bullet: the routing
  * metadata is built on the GPU inside the same submission as the expert
  * matrices; section "What Lily actually does": k routed experts plus the
- * shared expert per token).  For small batches (1 <= T <= 8 and T*k <= 512)
+ * shared expert per token).  For small batches (1 <= T <= 32 and T*k <= 512)
  * the routing is computed inside the matrix-vector kernels (every field of
  * *out is still written, identical to moe_route's). */
 MOE_API moe_status moe_layer(const moe_dims *dims, const float *logits, const uint16_t *x,
@@ -230,7 +230,7 @@ MOE_API moe_status moe_layer_noalloc(const moe_dims *dims, const float *logits, 
                                      void *stream);
 
 /* Host-only, pure.  Number of kernels one moe_layer call launches for these
- * dims, in launch order: small batches (1 <= T <= 8, T*k <= 512): decode
+ * dims, in launch order: small batches (1 <= T <= 32, T*k <= 512): decode
  * gate/up (with routing), decode down; larger T: route top-k, route scan,
  * route scatter, gate/up GEMM, down GEMM (routed and shared rows), combine;
  * T == 0: empty routing.  0 for invalid dims. */

@@ -127,12 +127,12 @@ def test_null_pointers_and_small_workspace_are_rejected():
 
 
 def test_kernel_counts_of_each_path():
-    """1 <= T <= 8 with T*k <= 512: two kernels (decode gate/up with routing,
+    """1 <= T <= 32 with T*k <= 512: two kernels (decode gate/up with routing,
     decode down); larger batches: three routing kernels and three GEMM-path
     kernels; T = 0: one."""
     base = dict(d=256, E=128, F=128, Fs=128, G=64)
-    for T, k, n in [(1, 8, 2), (1, 17, 2), (2, 8, 2), (8, 8, 2), (8, 64, 2), (9, 8, 6), (8, 65, 6),
-                    (4096, 8, 6), (0, 8, 1)]:
+    for T, k, n in [(1, 8, 2), (1, 17, 2), (2, 8, 2), (8, 8, 2), (8, 64, 2), (9, 8, 2), (8, 65, 6),
+                    (16, 8, 2), (32, 16, 2), (32, 17, 6), (33, 8, 6), (4096, 8, 6), (0, 8, 1)]:
         dm = B.make_dims(wl.Dims(T=T, k=k, **base))
         assert B.moe_layer_kernels(dm) == n, (T, k)
 

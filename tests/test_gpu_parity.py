@@ -26,8 +26,11 @@ SMALL = {
     "T2_smallest_gemm": (wl.Dims(T=2, d=128, E=8, k=2, F=64, Fs=64, G=32), False),
     "zipf_T500_E64_k6": (wl.Dims(T=500, d=128, E=64, k=6, F=64, Fs=64, G=32), True),
     "T1_small_decode": (wl.Dims(T=1, d=256, E=16, k=4, F=128, Fs=192, G=64), False),
-    # small batches (2 <= T <= 8, T k <= 512) take the matrix-vector kernels
+    # small batches (2 <= T <= 32, T k <= 512) take the matrix-vector kernels
     "T5_small_batch": (wl.Dims(T=5, d=256, E=16, k=4, F=128, Fs=192, G=64), False),
+    "T16_small_batch": (wl.Dims(T=16, d=256, E=16, k=4, F=128, Fs=192, G=64), False),
+    "T32_k16_batch_limit": (wl.Dims(T=32, d=128, E=64, k=16, F=64, Fs=64, G=32), False),
+    "T33_over_T_limit": (wl.Dims(T=33, d=128, E=16, k=2, F=64, Fs=64, G=32), False),
     "T8_k64_batch_limit": (wl.Dims(T=8, d=128, E=64, k=64, F=64, Fs=64, G=32), False),
     "T8_k65_over_limit": (wl.Dims(T=8, d=128, E=80, k=65, F=64, Fs=64, G=32), False),
     # many rows per expert: several full 128-row tiles per expert,
@@ -282,7 +285,7 @@ def test_decode_tie_heavy_logits(seed):
         check_y(c, g, ref)
 
 
-@pytest.mark.parametrize("T", [2, 3, 5, 8])
+@pytest.mark.parametrize("T", [2, 3, 5, 8, 9, 16, 31, 32])
 def test_small_batch_full_size(T):
     """Few-token batches at the workload's layer shape: every token of every
     slot, routing outputs bit-exact in both the fused and the split call."""
@@ -294,11 +297,12 @@ def test_small_batch_full_size(T):
         check_y(c, g, ref)
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_small_batch_tie_heavy_logits(seed):
-    """T = 6, logits in {-1, -0, 0, 1}: tokens share experts and tie inside
-    the top 8, so the batch's stable sorted order and tiles are exercised."""
-    dims = wl.Dims(T=6, d=256, E=32, k=8, F=128, Fs=128, G=64)
+@pytest.mark.parametrize("T,seed", [(6, 0), (6, 1), (32, 2)])
+def test_small_batch_tie_heavy_logits(T, seed):
+    """Logits in {-1, -0, 0, 1}: tokens share experts and tie inside the top
+    8, so the batch's stable sorted order and tiles are exercised (T = 32:
+    up to 32 rows of one expert in one tile)."""
+    dims = wl.Dims(T=T, d=256, E=32, k=8, F=128, Fs=128, G=64)
     c = wl.make_case(dims, seed=500 + seed)
     rng = np.random.default_rng(50 + seed)
     L = rng.integers(-1, 2, (dims.T, dims.E)).astype(np.float32)
