@@ -62,25 +62,6 @@ constexpr int kBRow = 64;                         // bytes of codes per B row pe
 constexpr int kBWave = 64 * kBRow;                // 4 KB per wave
 constexpr int kBBuf = 4 * kBWave;                 // 16 KB per buffer
 
-// One 16-byte-per-lane global->LDS copy (global_load_lds_dwordx4, LDS base in
-// M0) from base + voff: a wave-uniform 64-bit base in SGPRs and a 32-bit
-// per-lane byte offset, so a row address costs one VGPR instead of two.
-// Issued from inline assembly so that the compiler does not treat LDS reads
-// of the other buffers as dependent on it (it would wait for every copy in
-// flight before each of them); the main loop counts these copies itself
-// (wait_vmcnt).  No memory clobber: a copy writes an LDS buffer that no wave
-// reads until after the next block_sync, whose compiler fences keep every
-// LDS access on its side of the barrier, so the LDS reads of the current
-// step may be scheduled freely around the copies.  The s_nop covers both the
-// M0 write and a base just moved into SGPRs by a VALU readfirstlane.
-__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint8_t *lds)
-{
-    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds);
-    const uint64_t sb = uniform_u64((uint64_t)(uintptr_t)base);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(sb)
-                 : "m0");
-}
-
 // Copy the A tile of K step kt (MS*32 rows x 64 bf16) into an A stage:
 // wave w, copy i moves rows 8 (4 i + w) .. +7, 8 lanes per 128-byte row.
 // aoff[i] is this lane's byte offset (source row, chunk) from abase for copy

@@ -1,4 +1,5 @@
-// Pieces shared by the grouped-GEMM kernels of the prefill path (gfx950):
+// Pieces shared by the matrix-core kernels of the prefill path (grouped GEMMs
+// and router projection, gfx950):
 // kernel arguments, XCD-aware block order, explicit memory-counter waits, the
 // fence-free workgroup barrier, scale/bias words of a pair of K steps and the
 // register decode of eight 4-bit codes into a bf16 MFMA operand.
@@ -95,6 +96,25 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v)
 // an offset that is the same in every lane, moved to SGPRs (applied to
 // offsets rather than pointers, which keeps the pointers' address space)
 __device__ __forceinline__ size_t uniform_size(size_t v) { return (size_t)uniform_u64((uint64_t)v); }
+
+// One 16-byte-per-lane global->LDS copy (global_load_lds_dwordx4, LDS base in
+// M0) from base + voff: a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset, so a row address costs one VGPR instead of two.
+// Issued from inline assembly so that the compiler does not treat LDS reads
+// of the other buffers as dependent on it (it would wait for every copy in
+// flight before each of them); the main loop counts these copies itself
+// (wait_vmcnt).  No memory clobber: a copy writes an LDS buffer that no wave
+// reads until after the next block_sync, whose compiler fences keep every
+// LDS access on its side of the barrier, so the LDS reads of the current
+// step may be scheduled freely around the copies.  The s_nop covers both the
+// M0 write and a base just moved into SGPRs by a VALU readfirstlane.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint8_t *lds)
+{
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds);
+    const uint64_t sb = uniform_u64((uint64_t)(uintptr_t)base);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(sb)
+                 : "m0");
+}
 
 // wait until at most N vector-memory operations of this wave are in flight
 template <int N>

@@ -11,22 +11,21 @@
 // rows, then lo rows), expert-major so that each lane's MFMA operand is 16
 // contiguous bytes; Epad = E rounded up to 64, padding rows zero.
 //
-// router_gemm_kernel: one block = 256 tokens x 64 experts over a K range,
-// each wave 64 tokens (two 32-token tiles) x the block's 64 experts (two
-// 32-expert tiles).  The router rows of the block (hi and lo, 64 experts x
-// a 64-wide K chunk, 16 KB) are staged in LDS, double-buffered, and shared
-// by the four waves -- each router row is read from L2 once per 256 tokens;
-// each wave loads its activation fragments from global memory one chunk
-// ahead.  v_mfma_f32_32x32x16_bf16 with the router as the first operand, so
-// lane l holds token l % 32 of a token tile and register r of an expert tile
-// holds expert 8 (r / 4) + 4 (l / 32) + r % 4 of it.  When the grid would be
-// small, K is split into KS ranges whose partial logits a second kernel sums
-// in range order (deterministic), adding the bias; with KS = 1 the GEMM
-// writes the logits itself.
+// router_gemm_kernel: one block = 128 tokens x 64 experts over a K range,
+// each wave 32 tokens x the block's 64 experts (two 32-expert tiles).  Per
+// 64-wide K chunk the block's router rows (hi and lo, 64 experts, 16 KB) and
+// each wave's 32 activation rows (4 KB) are copied global -> LDS
+// (global_load_lds_dwordx4) three chunks ahead into a ring of four stages;
+// each router row is read from L2 once per 128 tokens.  v_mfma_f32_32x32x16
+// _bf16 with the router as the first operand, so lane l holds token l % 32 of
+// the wave's tile and register r of an expert tile holds expert 8 (r / 4) +
+// 4 (l / 32) + r % 4 of it.  When the grid would be small, K is split into
+// KS ranges whose partial logits a second kernel sums in range order
+// (deterministic), adding the bias; with KS = 1 the GEMM writes the logits
+// itself.
 #include <type_traits>
 
-#include "moe_device.h"
-#include "moe_internal.h"
+#include "gemm_common.h"
 
 namespace moe {
 
@@ -46,8 +45,10 @@ __global__ __launch_bounds__(256) void router_pack_kernel(const float *__restric
     P[n + idx] = lo;
 }
 
-constexpr int kRtTok = 256;  // tokens per block
-constexpr int kRtK = 64;     // K chunk per LDS stage
+constexpr int kRtTok = 128;    // tokens per block
+constexpr int kRtK = 64;       // K chunk per LDS stage
+constexpr int kRtStages = 4;   // LDS ring: chunks c .. c + 3 in flight
+constexpr int kRtMinChunks = 8;  // K chunks per block at least, when K is split
 
 struct RouterArgs {
     const uint16_t *x;    // [T][d]
@@ -55,116 +56,97 @@ struct RouterArgs {
     const float *bias;    // [E] or null
     float *out;           // KS == 1: logits [T][E]; else partials [KS][T][E]
     int T, d, E, Epad, KS, kper;
-    int ntb, net;         // token blocks (256), expert tiles (64)
+    int ntb, net;         // token blocks (128), expert tiles (64)
 };
 
-// LDS stage: [hi/lo][64 experts][64 K] bf16, the eight 16-byte chunks of
-// expert row e stored at slot c ^ (e & 7) (spreads the operand reads, 32
-// rows x one chunk, over the banks)
-struct RtStage {
-    uint4 v[2][64][8];
-};
+// Router stage: [hi/lo][64 experts][8 chunks of 16 B], chunk kc of expert row
+// e at slot kc ^ ((e >> 1) & 7).  Activation stage of a wave: [32 tokens][8
+// chunks of 16 B], chunk kc of token row t at slot kc ^ ((t >> 1) & 7).  Both
+// keep the operand reads (32 rows x one chunk) free of bank conflicts.
+constexpr int kRtWStage = 2 * 64 * 128;  // 16 KB
+constexpr int kRtXWave = 32 * 128;       // 4 KB
 
 __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs a)
 {
-    __shared__ RtStage st[2];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    __shared__ __attribute__((aligned(1024))) uint8_t wst[kRtStages][kRtWStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t xst[kRtStages][4][kRtXWave];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int per = a.ntb * a.net;
     const int ks = blockIdx.x / per;
     const int rem = blockIdx.x - ks * per;
     const int et = rem / a.ntb, tb = rem - et * a.ntb;
     const int n = lane & 31, h = lane >> 5;
-    const size_t EP = (size_t)a.Epad * a.d;
-    // this thread's share of a stage: chunks c = tid + 256 i, i < 4, of the
-    // 1024 (hi/lo, expert row, 16-byte chunk) of a stage
-    const uint16_t *wsrc[4];
-    int wdst_hl[4], wdst_e[4], wdst_s[4];
+    // router copies: copy i of wave w fills the 16-byte positions 64 (4 i + w)
+    // + lane of a stage, i.e. (hi/lo, expert row, slot) = (p >> 9, (p >> 3) &
+    // 63, p & 7); byte offsets from P at the block's first K column
+    uint32_t woff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i;
-        const int hl = c >> 9, e = (c >> 3) & 63, kc = c & 7;
-        wsrc[i] = a.P + hl * EP + (size_t)(64 * et + e) * a.d + 8 * kc;
-        wdst_hl[i] = hl; wdst_e[i] = e; wdst_s[i] = kc ^ (e & 7);
+        const int p = 64 * (4 * i + wave) + lane;
+        const int hl = p >> 9, e = (p >> 3) & 63, kc = (p & 7) ^ ((e >> 1) & 7);
+        woff[i] = (uint32_t)(((size_t)hl * a.Epad + 64 * et + e) * a.d * 2 + 16 * kc);
     }
-    // this lane's activation rows (two token tiles); rows past T load a valid row
-    const uint16_t *xr[2];
-    int tok[2];
+    // activation copies: copy j fills rows 8 j + lane / 8 of the wave's stage,
+    // slot lane & 7; rows past T load a valid row
+    uint32_t xoff[4];
+    int tok0 = kRtTok * tb + 32 * wave;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        tok[u] = kRtTok * tb + 64 * wave + 32 * u + n;
-        xr[u] = a.x + (size_t)min(tok[u], a.T - 1) * a.d + 8 * h;
+    for (int j = 0; j < 4; ++j) {
+        const int row = 8 * j + (lane >> 3);
+        const int kc = (lane & 7) ^ ((row >> 1) & 7);
+        xoff[j] = (uint32_t)min(tok0 + row, a.T - 1) * (uint32_t)a.d * 2u + 16u * (uint32_t)kc;
     }
-    f32x16 acc[2][2];  // [token tile][expert tile]
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int v = 0; v < 2; ++v)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[u][v][r] = 0.f;
-
     const int k0 = ks * a.kper, nch = a.kper / kRtK;
-    uint4 wreg[4];
-    bf16x8 xa[2][2][4];  // [buffer][token tile][sub-step]
-    auto load_w = [&](int kc) __attribute__((always_inline)) {
+    auto issue = [&](int c, int stage) __attribute__((always_inline)) {
+        const uint16_t *wb = a.P + k0 + c * kRtK, *xb = a.x + k0 + c * kRtK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wreg[i] = *reinterpret_cast<const uint4 *>(wsrc[i] + kc);
+        for (int i = 0; i < 4; ++i) dma16(wb, woff[i], &wst[stage][(4 * i + wave) * 1024]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(xb, xoff[j], &xst[stage][wave][j * 1024]);
     };
-    auto store_w = [&](int b) __attribute__((always_inline)) {
+    f32x16 acc[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[b].v[wdst_hl[i]][wdst_e[i]][wdst_s[i]] = wreg[i];
-    };
-    auto load_x = [&](int b, int kc) __attribute__((always_inline)) {
+    for (int v = 0; v < 2; ++v)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int r = 0; r < 16; ++r) acc[v][r] = 0.f;
+
+    // prologue: chunks 0 .. kRtStages - 2; every step issues one more chunk
+    // (clamped to the last one past the end, so that the counts stay uniform)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) xa[b][u][q] = *reinterpret_cast<const bf16x8 *>(xr[u] + kc + 16 * q);
-    };
-    load_w(k0);
-    load_x(0, k0);
-    store_w(0);
-    __syncthreads();
-    // chunk c computes from stage c % 2 and activation buffer c % 2 while the
-    // next chunk's router rows and activations are loaded
-    auto chunk = [&](auto bc, int c) __attribute__((always_inline)) {
-        constexpr int b = decltype(bc)::value;
-        const bool more = c + 1 < nch;
-        if (more) {
-            load_w(k0 + (c + 1) * kRtK);
-            load_x(b ^ 1, k0 + (c + 1) * kRtK);
-        }
+    for (int c = 0; c < kRtStages - 1; ++c) issue(min(c, nch - 1), c);
+    for (int c = 0; c < nch; ++c) {
+        const int s = c % kRtStages;
+        wait_vmcnt<8 * (kRtStages - 2)>();  // this wave's copies of chunk c have landed
+        block_sync();                         // ... and every wave's
+        issue(min(c + kRtStages - 1, nch - 1), (c + kRtStages - 1) % kRtStages);  // the stage of chunk c - 1
+        const uint8_t *ws = wst[s], *xs = xst[s][wave];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {  // 16-wide sub-steps of the chunk
-            const int slot_h = 2 * q + h;
+        for (int q = 0; q < 4; ++q) {  // 16-wide sub-steps: chunk 2 q + h of a row
+            const int kc = 2 * q + h;
+            const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xs + n * 128 + 16 * (kc ^ ((n >> 1) & 7)));
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
                 const int e = 32 * v + n;
-                const bf16x8 wh = __builtin_bit_cast(bf16x8, st[b].v[0][e][slot_h ^ (e & 7)]);
-                const bf16x8 wlo = __builtin_bit_cast(bf16x8, st[b].v[1][e][slot_h ^ (e & 7)]);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    acc[u][v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, xa[b][u][q], acc[u][v], 0, 0, 0);
-                    acc[u][v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wlo, xa[b][u][q], acc[u][v], 0, 0, 0);
-                }
+                const int off = e * 128 + 16 * (kc ^ ((e >> 1) & 7));
+                const bf16x8 wh = *reinterpret_cast<const bf16x8 *>(ws + off);
+                const bf16x8 wl = *reinterpret_cast<const bf16x8 *>(ws + 64 * 128 + off);
+                acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, xv, acc[v], 0, 0, 0);
+                acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, xv, acc[v], 0, 0, 0);
             }
         }
-        if (more) store_w(b ^ 1);  // stage b ^ 1 was last read before the previous barrier
-        __syncthreads();
-    };
-    for (int c = 0; c < nch; c += 2) {
-        chunk(std::integral_constant<int, 0>(), c);
-        if (c + 1 < nch) chunk(std::integral_constant<int, 1>(), c + 1);
     }
+    wait_vmcnt<0>();  // no copy into LDS outlives the block
     const bool direct = a.KS == 1;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        if (tok[u] >= a.T) continue;
-        float *orow = a.out + ((size_t)ks * a.T + tok[u]) * a.E;
+    const int t = tok0 + n;
+    if (t < a.T) {
+        float *orow = a.out + ((size_t)ks * a.T + t) * a.E;
 #pragma unroll
         for (int v = 0; v < 2; ++v)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int e = 64 * et + 32 * v + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (e < a.E) orow[e] = acc[u][v][r] + ((direct && a.bias) ? a.bias[e] : 0.f);
+                if (e < a.E) orow[e] = acc[v][r] + ((direct && a.bias) ? a.bias[e] : 0.f);
             }
     }
 }
@@ -184,13 +166,14 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float *__restr
 
 int router_epad(int E) { return (E + 63) & ~63; }
 
-// K ranges: enough waves to spread a small batch over the chip (about 1024),
-// each range a whole number of 16-wide K steps
+// K ranges: split until the grid has a block per compute unit (256), each
+// range a whole number of K chunks and at least kRtMinChunks of them
 int router_splits(int T, int d, int E)
 {
     const int64_t blocks = (int64_t)((T + kRtTok - 1) / kRtTok) * (router_epad(E) / 64);
+    const int nch = d / kRtK;
     int ks = 1;
-    while (ks < 16 && blocks * ks * 2 <= 512 && (d / kRtK) % (ks * 2) == 0) ks *= 2;
+    while (blocks * ks < 256 && nch % (ks * 2) == 0 && nch / (ks * 2) >= kRtMinChunks) ks *= 2;
     return ks;
 }
 
