@@ -224,12 +224,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
 
 // One block = kDownRows output rows of token blockIdx.y; lane chunks
 // c = tid, tid + blockDim, ... of [h_s, h_0 .. h_{k-1}] in 32-element chunks.
+// Row blocks are spread over the XCDs in contiguous ranges, so that the
+// blocks reading one 128-byte line of scales or biases (8 rows) share an L2.
 __global__ __launch_bounds__(kDownMaxThreads) void decode_down_kernel(DecodeArgs a)
 {
     __shared__ float red[kDownMaxThreads / kWave][kDownRows];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nw = blockDim.x >> 6;
-    const int row0 = blockIdx.x * kDownRows;
+    const int rb = xcd_logical_block(blockIdx.x, (a.d + kDownRows - 1) / kDownRows);
+    if (rb < 0) return;  // grid padding (block-uniform)
+    const int row0 = rb * kDownRows;
     const int t = blockIdx.y;
     const int cF = a.F >> 5, cFs = a.Fs >> 5;
     const int nchunks = a.k * cF + cFs;
@@ -324,7 +328,7 @@ hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
     const int nchunks = p.k * (p.F >> 5) + (p.Fs >> 5);
     int nw = (nchunks + kWave - 1) / kWave;
     nw = nw < 1 ? 1 : (nw > kDownMaxThreads / kWave ? kDownMaxThreads / kWave : nw);
-    const int nb2 = (p.d + kDownRows - 1) / kDownRows;
+    const int nb2 = ((p.d + kDownRows - 1) / kDownRows + 7) & ~7;  // a multiple of 8 (XCD ranges)
     launch(tr, decode_down_kernel, dim3(nb2, p.T), dim3(nw * kWave), 0, s, a);
     return hipGetLastError();
 }

@@ -66,21 +66,6 @@ __device__ __forceinline__ int perm_at(const int32_t *perm, int p, int A)
     return (int)min((uint32_t)perm[p], (uint32_t)(A - 1));
 }
 
-// Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
-// b % 8).  The grid is sized for the largest possible tile count, while the
-// count of blocks with work is known only on the device.  Give each XCD an
-// equal contiguous range of the blocks that have work, so that consecutive
-// logical blocks (the column blocks of one tile, then the next tile of the
-// same expert) run on the same XCD and share its L2.  -1: no work.
-__device__ __forceinline__ int xcd_logical_block(int bid, int total)
-{
-    const int per = (total + 7) >> 3;
-    const int i = bid >> 3;
-    if (i >= per) return -1;
-    const int L = (bid & 7) * per + i;
-    return L < total ? L : -1;
-}
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // A 64-bit integer that is the same in every lane, moved to SGPRs.  The

@@ -94,6 +94,22 @@ __device__ __forceinline__ float dot8_codes(uint32_t v, const float *x, float ac
     return acc;
 }
 
+// Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8).  Give each XCD an equal contiguous range of the `total` logical
+// blocks, so that consecutive logical blocks (the column blocks of one GEMM
+// tile, then the next tile of the same expert; neighbouring output rows of
+// a matrix-vector product) run on the same XCD and share its L2.  The grid
+// must hold at least 8 ceil(total / 8) blocks (a multiple of 8 >= total);
+// -1: a padding block with no work.
+__device__ __forceinline__ int xcd_logical_block(int bid, int total)
+{
+    const int per = (total + 7) >> 3;
+    const int i = bid >> 3;
+    if (i >= per) return -1;
+    const int L = (bid & 7) * per + i;
+    return L < total ? L : -1;
+}
+
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp_f32(float v)
 {
