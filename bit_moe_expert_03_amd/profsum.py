@@ -14,6 +14,9 @@ Usage (from the repository root):
     python -m bit_moe_expert_03_amd.profsum trace DB --cmd "..." --title "..."
     python -m bit_moe_expert_03_amd.profsum traffic --fetch DIR --write DIR \\
         --copy-kernel SUBSTRING --copy-bytes N --kernel NAME=SRC[,SRC...] ... --out FILE.json
+  NAME: KEY or KEY@MATCH; MATCH (default KEY) is a substring of exactly one
+  "kernel [grid N]" name (N workgroups), so a kernel launched with several
+  grids needs its grid in MATCH; KEY names the entry in the JSON.
 """
 from __future__ import annotations
 
@@ -67,8 +70,9 @@ def short_name(name: str) -> str:
 
 
 def counter_means(csv_dir, counter):
-    """Mean value of one counter per dispatch, per kernel (short name).  A
-    counter reported per hardware instance is summed over instances first."""
+    """Mean value of one counter per dispatch, per kernel and launch shape
+    (short name + " [grid N]", N workgroups).  A counter reported per hardware
+    instance is summed over instances first."""
     per = collections.defaultdict(lambda: collections.defaultdict(float))
     files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -78,7 +82,9 @@ def counter_means(csv_dir, counter):
             for r in csv.DictReader(fh):
                 if r["Counter_Name"] != counter:
                     continue
-                per[short_name(r["Kernel_Name"])][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+                wg = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+                key = f"{short_name(r['Kernel_Name'])} [grid {wg}]"
+                per[key][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
@@ -101,8 +107,8 @@ def cmd_traffic(a):
 
     def pick(table, sub):
         hits = [k for k in table if sub in k]
-        if not hits:
-            raise SystemExit(f"no kernel matching {sub!r}; have {sorted(table)}")
+        if len(hits) != 1:
+            raise SystemExit(f"{len(hits)} kernels match {sub!r} (name [grid N] must be unique); have {sorted(table)}")
         return table[hits[0]], hits[0]
 
     cf, cname = pick(fetch, a.copy_kernel)
@@ -114,9 +120,10 @@ def cmd_traffic(a):
     for spec in a.kernel:
         name, srcs = spec.split("=", 1)
         srcs = srcs.split(",")
-        f, full = pick(fetch, name)
-        w, _ = pick(write, name)
-        out["kernels"][name] = {"matched": full, "fetch_kib": f, "write_kib": w,
+        key, _, match = name.partition("@")
+        f, full = pick(fetch, match or key)
+        w, _ = pick(write, match or key)
+        out["kernels"][key] = {"matched": full, "fetch_kib": f, "write_kib": w,
                                 "fetch_bytes": f * 1024.0 * fscale, "write_bytes": w * 1024.0 * wscale,
                                 "traffic_bytes": f * 1024.0 * fscale + w * 1024.0 * wscale,
                                 "sources": srcs, "source_sha256": source_hash(srcs)}
