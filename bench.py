@@ -251,12 +251,8 @@ def bench_decode(B, wl, args):
     flush = CacheFlush()
     sec, per_kernel = run_timed(B, dm, calls, args.steps, args.warmup, flush)
     value = args.steps / sec
-    if len(per_kernel) == 1:  # one-launch decode: the kernel is the whole layer
-        names, kernel = ["decode_fused"], "decode_fused_kernel"
-        dom_bytes = decode_layer_bytes(dims) + dims.E * 4
-    else:
-        names, kernel = ["decode_gateup", "decode_down"], "decode_gateup_kernel"
-        dom_bytes = gateup_decode_bytes(dims)
+    names, kernel = ["decode_gateup", "decode_down"], "decode_gateup_kernel"
+    dom_bytes = gateup_decode_bytes(dims)
     dom_ms = per_kernel[0]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     out = {
