@@ -230,7 +230,7 @@ struct StepCopies {
 // next step are read from LDS (bnext, step jn of its pair) and its first
 // sub-step is decoded, so the next step starts with matrix-core work.  The
 // copies for later steps are spread over the sub-steps (cp).
-template <int MS, int G, bool B>
+template <int MS, int G, bool B, bool WAITB>
 __device__ __forceinline__ void kstep(const uint8_t *astage, const StepCodes &cur, const StepScales &sc,
                                       const FirstOps &first, const uint8_t *bnext, SBPair<G> &sbnext, int jn,
                                       StepCodes &nxt, FirstOps &nfirst, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS],
@@ -263,6 +263,9 @@ __device__ __forceinline__ void kstep(const uint8_t *astage, const StepCodes &cu
             o0[nx] = decode_sub(cur.w0[s + 1], sc.s0, sc.b0);
             o1[nx] = decode_sub(cur.w1[s + 1], sc.s1, sc.b1);
         } else {
+            // two code buffers: the codes of the next pair were copied during
+            // the previous step; the MS A copies of this step may stay in flight
+            if constexpr (WAITB) wait_vmcnt<MS>();
             read_codes(bnext, jn, nxt);
             // the next pair's scales are consumed here and not earlier: their
             // loads may still be in flight before this point
@@ -336,24 +339,24 @@ struct NoEpilogue {
 // multiple of nk, always a J = 1 step); its stores are in the vector-memory
 // count, so the entry wait of the next step (J = 0: everything) also covers
 // them.
-template <int MS, int G, int ST, class Epi>
+template <int MS, int G, int NB, int ST, class Epi>
 __device__ __forceinline__ void mainloop_step(int kt, const LoopShape &ls, const uint16_t *abase,
                                               const uint32_t (&aoff)[MS], const BSrc &bsrc, const LdsBufs &L,
                                               Carry<G> &cs, f32x16 (&acc0)[MS], f32x16 (&acc1)[MS], const Epi &epi)
 {
-    constexpr int J = ST & 1, PB = (ST >> 1) % 3;
+    constexpr int J = ST & 1, PB = (ST >> 1) % NB;
     if constexpr (J == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
     block_sync();
     if constexpr (J == 0) sb_load<G>(cs.sbn, bsrc, min((kt >> 1) + 1, ls.npair - 1));
     const StepCopies<MS, J == 0> cp = {abase + (min(kt + 1, ls.nt - 1) & ls.kmask) * kKStep, aoff, L.a<J ^ 1>(),
-                                       bsrc, b_offset(bsrc, min((kt >> 1) + 2, ls.npair - 1)),
-                                       L.b<(PB + 2) % 3>()};
+                                       bsrc, b_offset(bsrc, min((kt >> 1) + NB - 1, ls.npair - 1)),
+                                       L.b<(PB + NB - 1) % NB>()};
     // next step: same pair at J = 0, first step of the next pair at J = 1
-    constexpr int PBN = J == 0 ? PB : (PB + 1) % 3;
+    constexpr int PBN = J == 0 ? PB : (PB + 1) % NB;
     const StepCodes cur = cs.codes;
     const FirstOps first = cs.first;
     const StepScales sc = step_scales<G>(cs.sb, J);
-    kstep<MS, G, J == 0>(L.a<J>(), cur, sc, first, L.b<PBN>(), J == 0 ? cs.sb : cs.sbn, J ^ 1, cs.codes, cs.first,
+    kstep<MS, G, J == 0, NB == 2 && J == 1>(L.a<J>(), cur, sc, first, L.b<PBN>(), J == 0 ? cs.sb : cs.sbn, J ^ 1, cs.codes, cs.first,
                          acc0, acc1, cp);
     if constexpr (J == 1) cs.sb = cs.sbn;
     if constexpr (J == 1 && !std::is_same<Epi, NoEpilogue>::value) {
@@ -372,7 +375,7 @@ __device__ __forceinline__ void mainloop_step(int kt, const LoopShape &ls, const
 // 6 steps: the loop body is 6 straight-line steps, and 1 to 5 remaining
 // steps run the same instantiations under conditions.  Past the end, copies
 // re-load valid data instead of branching.
-template <int MS, int G, class Epi = NoEpilogue>
+template <int MS, int G, int NB, class Epi = NoEpilogue>
 __device__ __forceinline__ void mainloop(const uint16_t *abase, const uint32_t (&aoff)[MS], const LoopShape &ls,
                                          const BSrc &bsrc, const LdsBufs &L, f32x16 (&acc0)[MS],
                                          f32x16 (&acc1)[MS], const Epi &epi = Epi())
@@ -387,26 +390,38 @@ __device__ __forceinline__ void mainloop(const uint16_t *abase, const uint32_t (
     sb_load<G>(cs.sb, bsrc, 0);
     a_dma<MS>(abase, aoff, 0, L.a<0>());
     b_dma(bsrc, 0, L.b<0>());
-    b_dma(bsrc, min(1, ls.npair - 1), L.b<1>());
+    if constexpr (NB == 3) b_dma(bsrc, min(1, ls.npair - 1), L.b<1>());
     wait_vmcnt<0>();
     block_sync();
     read_codes(L.b<0>(), 0, cs.codes);
     decode_first(cs.codes, step_scales<G>(cs.sb, 0), cs.first);
 
     int kt = 0;
-    for (; kt + 5 < nk; kt += 6) {
-        mainloop_step<MS, G, 0>(kt, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
-        mainloop_step<MS, G, 1>(kt + 1, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
-        mainloop_step<MS, G, 2>(kt + 2, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
-        mainloop_step<MS, G, 3>(kt + 3, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
-        mainloop_step<MS, G, 4>(kt + 4, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
-        mainloop_step<MS, G, 5>(kt + 5, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+    if constexpr (NB == 3) {
+        for (; kt + 5 < nk; kt += 6) {
+            mainloop_step<MS, G, NB, 0>(kt, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+            mainloop_step<MS, G, NB, 1>(kt + 1, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+            mainloop_step<MS, G, NB, 2>(kt + 2, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+            mainloop_step<MS, G, NB, 3>(kt + 3, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+            mainloop_step<MS, G, NB, 4>(kt + 4, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+            mainloop_step<MS, G, NB, 5>(kt + 5, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        }
+        if (kt < nk) mainloop_step<MS, G, NB, 0>(kt, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        if (kt + 1 < nk) mainloop_step<MS, G, NB, 1>(kt + 1, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        if (kt + 2 < nk) mainloop_step<MS, G, NB, 2>(kt + 2, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        if (kt + 3 < nk) mainloop_step<MS, G, NB, 3>(kt + 3, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        if (kt + 4 < nk) mainloop_step<MS, G, NB, 4>(kt + 4, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+    } else {
+        for (; kt + 3 < nk; kt += 4) {
+            mainloop_step<MS, G, NB, 0>(kt, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+            mainloop_step<MS, G, NB, 1>(kt + 1, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+            mainloop_step<MS, G, NB, 2>(kt + 2, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+            mainloop_step<MS, G, NB, 3>(kt + 3, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        }
+        if (kt < nk) mainloop_step<MS, G, NB, 0>(kt, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        if (kt + 1 < nk) mainloop_step<MS, G, NB, 1>(kt + 1, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
+        if (kt + 2 < nk) mainloop_step<MS, G, NB, 2>(kt + 2, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
     }
-    if (kt < nk) mainloop_step<MS, G, 0>(kt, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
-    if (kt + 1 < nk) mainloop_step<MS, G, 1>(kt + 1, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
-    if (kt + 2 < nk) mainloop_step<MS, G, 2>(kt + 2, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
-    if (kt + 3 < nk) mainloop_step<MS, G, 3>(kt + 3, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
-    if (kt + 4 < nk) mainloop_step<MS, G, 4>(kt + 4, ls, abase, aoff, bsrc, L, cs, acc0, acc1, epi);
     wait_vmcnt<0>();  // no copy into LDS outlives the loop
 }
 
@@ -439,7 +454,7 @@ __device__ __forceinline__ void a_offsets(uint32_t (&aoff)[MS], int ld, const in
     }
 }
 
-template <int MS, int G>
+template <int MS, int G, int NB>
 __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int rows, int N,
                                             const moe_qmat &mg, const moe_qmat &mu, size_t ebase,
                                             uint16_t *out, bool routed, int nt, uint8_t *lds_a0,
@@ -468,7 +483,7 @@ __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int r
     src.ngroups = Kg;
     src.pshift = 30; src.cq = 0; src.cs = 0;
     f32x16 accg[MS], accu[MS];
-    mainloop<MS, G>(a.x, aoff, single_block_loop(a.d), src, L, accg, accu);
+    mainloop<MS, G, NB>(a.x, aoff, single_block_loop(a.d), src, L, accg, accu);
     // epilogue: h = bf16(silu(g) * u), one row per lane, 16-byte stores
     if (ncol0 < N) {
 #pragma unroll
@@ -482,14 +497,29 @@ __device__ __forceinline__ void gateup_body(const GateUpArgs &a, int row0, int r
     }
 }
 
+// Code buffers and blocks per CU by GEMM and tile height.  A 32-row down
+// block is short (F / 64 K steps per column block) and does one MFMA per
+// decoded operand, so its prologue and copy latency have little to hide
+// behind: it keeps two code buffers (codes one pair ahead, 40 KB of LDS)
+// so that four blocks share a CU.  Measured on the T = 512 workload (32-row
+// tiles): down GEMM 57 -> 52 us; the gate/up GEMM (32 K steps) ran slower
+// that way (116 -> 156 us) and keeps three buffers and two blocks per CU.
+template <int BM, bool DOWN> constexpr int code_buffers() { return BM == 32 && DOWN ? 2 : 3; }
+template <int BM, bool DOWN> constexpr int blocks_per_cu() { return BM == 32 && DOWN ? 4 : 2; }
+
 template <int BM, int G>
-__global__ __launch_bounds__(kGemmThreads, 2) void moe_gateup_kernel(GateUpArgs a)
+__global__ __launch_bounds__(kGemmThreads, (blocks_per_cu<BM, false>())) void moe_gateup_kernel(GateUpArgs a)
 {
+    constexpr int kNB = code_buffers<BM, false>();
     __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[BM * kARow];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[BM * kARow];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kBBuf];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_b2[kBBuf];
+    uint8_t *lds_b2 = lds_b1;  // unused with two code buffers
+    if constexpr (kNB == 3) {
+        __shared__ __attribute__((aligned(1024))) uint8_t lds_b2x[kBBuf];
+        lds_b2 = lds_b2x;
+    }
     const int nblk_r = max(0, min(*a.tiles.num_tiles, a.tiles.max_tiles)) * a.ntn_r;  // routed blocks with work
     const int L = xcd_logical_block(blockIdx.x, nblk_r + a.nblk_s);
     if (L < 0) return;
@@ -520,11 +550,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gateup_kernel(GateUpArgs 
     }
     const int msub = (rows + 31) >> 5;  // live 32-row sub-tiles (block-uniform)
     if (BM >= 128 && msub > 2)
-        gateup_body<(BM >= 128 ? 4 : 1), G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+        gateup_body<(BM >= 128 ? 4 : 1), G, kNB>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
     else if (BM >= 64 && msub == 2)
-        gateup_body<(BM >= 64 ? 2 : 1), G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+        gateup_body<(BM >= 64 ? 2 : 1), G, kNB>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
     else
-        gateup_body<1, G>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+        gateup_body<1, G, kNB>(a, row0, rows, N, *mg, *mu, ebase, out, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
 }
 
 // Store 64 columns (this wave's share of a 256-column block) of the tile's
@@ -555,7 +585,7 @@ __device__ __forceinline__ void down_store(const DownArgs &a, const float (&wrow
 // the codes and scales move to the next block's rows, and each finished
 // block is stored from inside the loop, so the block's prologue (tile
 // lookup, routing weights, first copies) is paid once per NC blocks.
-template <int MS, int G, bool CHAIN>
+template <int MS, int G, bool CHAIN, int NB>
 __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows, int K,
                                           const moe_qmat &m, size_t ebase, const uint16_t *hsrc,
                                           int orow0, bool routed, int nt0, uint8_t *lds_a0,
@@ -600,22 +630,27 @@ __device__ __forceinline__ void down_body(const DownArgs &a, int row0, int rows,
         auto epi = [&](int c, auto &r0, auto &r1) __attribute__((always_inline)) {
             down_store<MS>(a, wrow, rows, orow0, ncol0 + 256 * c, r0, r1);
         };
-        mainloop<MS, G>(hsrc, aoff, ls, src, L, acc0, acc1, epi);
+        mainloop<MS, G, NB>(hsrc, aoff, ls, src, L, acc0, acc1, epi);
     } else {
         src.pshift = 30; src.cq = 0; src.cs = 0;
-        mainloop<MS, G>(hsrc, aoff, single_block_loop(K), src, L, acc0, acc1);
+        mainloop<MS, G, NB>(hsrc, aoff, single_block_loop(K), src, L, acc0, acc1);
         if (ncol0 < a.d) down_store<MS>(a, wrow, rows, orow0, ncol0, acc0, acc1);
     }
 }
 
 template <int BM, int G>
-__global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
+__global__ __launch_bounds__(kGemmThreads, (blocks_per_cu<BM, true>())) void moe_down_kernel(DownArgs a)
 {
+    constexpr int kNB = code_buffers<BM, true>();
     __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[BM * kARow];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[BM * kARow];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kBBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kBBuf];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_b2[kBBuf];
+    uint8_t *lds_b2 = lds_b1;  // unused with two code buffers
+    if constexpr (kNB == 3) {
+        __shared__ __attribute__((aligned(1024))) uint8_t lds_b2x[kBBuf];
+        lds_b2 = lds_b2x;
+    }
     const int ncb = a.ntn / a.nc;  // blocks per tile, each over a.nc column blocks
     const int nblk_r = max(0, min(*a.tiles.num_tiles, a.tiles.max_tiles)) * ncb;  // routed blocks with work
     const int L = xcd_logical_block(blockIdx.x, nblk_r + a.nblk_s);
@@ -649,18 +684,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_down_kernel(DownArgs a)
     const int msub = (rows + 31) >> 5;
     if (a.nc > 1) {
         if (BM >= 128 && msub > 2)
-            down_body<(BM >= 128 ? 4 : 1), G, true>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+            down_body<(BM >= 128 ? 4 : 1), G, true, kNB>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
         else if (BM >= 64 && msub == 2)
-            down_body<(BM >= 64 ? 2 : 1), G, true>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+            down_body<(BM >= 64 ? 2 : 1), G, true, kNB>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
         else
-            down_body<1, G, true>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+            down_body<1, G, true, kNB>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
     } else {
         if (BM >= 128 && msub > 2)
-            down_body<(BM >= 128 ? 4 : 1), G, false>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+            down_body<(BM >= 128 ? 4 : 1), G, false, kNB>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
         else if (BM >= 64 && msub == 2)
-            down_body<(BM >= 64 ? 2 : 1), G, false>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+            down_body<(BM >= 64 ? 2 : 1), G, false, kNB>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
         else
-            down_body<1, G, false>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
+            down_body<1, G, false, kNB>(a, row0, rows, K, *m, ebase, hsrc, orow0, routed, nt, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2);
     }
 }
 

@@ -15,7 +15,8 @@
 // each wave 32 tokens x the block's 64 experts (two 32-expert tiles).  Per
 // 64-wide K chunk the block's router rows (hi and lo, 64 experts, 16 KB) and
 // each wave's 32 activation rows (4 KB) are copied global -> LDS
-// (global_load_lds_dwordx4) three chunks ahead into a ring of four stages;
+// (global_load_lds_dwordx4) into a ring of four stages, four chunks ahead of
+// the MFMAs that use them;
 // each router row is read from L2 once per 128 tokens.  v_mfma_f32_32x32x16
 // _bf16 with the router as the first operand, so lane l holds token l % 32 of
 // the wave's tile and register r of an expert tile holds expert 8 (r / 4) +
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(256) void router_pack_kernel(const float *__restric
 
 constexpr int kRtTok = 128;    // tokens per block
 constexpr int kRtK = 64;       // K chunk per LDS stage
-constexpr int kRtStages = 4;   // LDS ring: chunks c .. c + 3 in flight
+constexpr int kRtStages = 4;   // LDS ring: chunks c + 1 .. c + 4 landed or in flight
 constexpr int kRtMinChunks = 8;  // K chunks per block at least, when K is split
 
 struct RouterArgs {
@@ -111,43 +112,109 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[v][r] = 0.f;
 
-    // prologue: chunks 0 .. kRtStages - 2; every step issues one more chunk
-    // (clamped to the last one past the end, so that the counts stay uniform)
+    // The operands of one chunk (per 16-wide sub-step q: the activation
+    // chunk 2 q + h of token n, router chunks of experts n and 32 + n, hi
+    // and lo) are read from LDS into registers one chunk ahead, so that the
+    // reads of chunk c + 1 are in flight under the MFMAs of chunk c: with
+    // one wave per SIMD nothing else hides the LDS latency of an operand
+    // read right before its MFMA.
+    struct ChunkOps {
+        bf16x8 x[4], w[4][2][2];  // [sub-step][expert tile][hi, lo]
+    };
+    auto read_ops = [&](int stage, ChunkOps &o) __attribute__((always_inline)) {
+        const uint8_t *ws = wst[stage], *xs = xst[stage][wave];
 #pragma unroll
-    for (int c = 0; c < kRtStages - 1; ++c) issue(min(c, nch - 1), c);
-    for (int c = 0; c < nch; ++c) {
-        const int s = c % kRtStages;
-        wait_vmcnt<8 * (kRtStages - 2)>();  // this wave's copies of chunk c have landed
-        block_sync();                         // ... and every wave's
-        issue(min(c + kRtStages - 1, nch - 1), (c + kRtStages - 1) % kRtStages);  // the stage of chunk c - 1
-        const uint8_t *ws = wst[s], *xs = xst[s][wave];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {  // 16-wide sub-steps: chunk 2 q + h of a row
+        for (int q = 0; q < 4; ++q) {
             const int kc = 2 * q + h;
-            const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xs + n * 128 + 16 * (kc ^ ((n >> 1) & 7)));
+            o.x[q] = *reinterpret_cast<const bf16x8 *>(xs + n * 128 + 16 * (kc ^ ((n >> 1) & 7)));
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
                 const int e = 32 * v + n;
                 const int off = e * 128 + 16 * (kc ^ ((e >> 1) & 7));
-                const bf16x8 wh = *reinterpret_cast<const bf16x8 *>(ws + off);
-                const bf16x8 wl = *reinterpret_cast<const bf16x8 *>(ws + 64 * 128 + off);
-                acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, xv, acc[v], 0, 0, 0);
-                acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, xv, acc[v], 0, 0, 0);
+                o.w[q][v][0] = *reinterpret_cast<const bf16x8 *>(ws + off);
+                o.w[q][v][1] = *reinterpret_cast<const bf16x8 *>(ws + 64 * 128 + off);
             }
         }
-    }
-    wait_vmcnt<0>();  // no copy into LDS outlives the block
-    const bool direct = a.KS == 1;
-    const int t = tok0 + n;
-    if (t < a.T) {
-        float *orow = a.out + ((size_t)ks * a.T + t) * a.E;
+    };
+    auto mfma_ops = [&](const ChunkOps &o) __attribute__((always_inline)) {
 #pragma unroll
-        for (int v = 0; v < 2; ++v)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int e = 64 * et + 32 * v + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (e < a.E) orow[e] = acc[v][r] + ((direct && a.bias) ? a.bias[e] : 0.f);
+            for (int v = 0; v < 2; ++v) {
+                acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[q][v][0], o.x[q], acc[v], 0, 0, 0);
+                acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[q][v][1], o.x[q], acc[v], 0, 0, 0);
             }
+    };
+
+    // prologue: chunks 0 .. kRtStages - 1 copied, chunk 0's operands read.
+    // Every iteration issues one more chunk (clamped to the last one past
+    // the end, so that the counts stay uniform).
+#pragma unroll
+    for (int c = 0; c < kRtStages; ++c) issue(min(c, nch - 1), c);
+    ChunkOps ops[2];
+    wait_vmcnt<8 * (kRtStages - 1)>();  // this wave's copies of chunk 0 have landed
+    block_sync();                         // ... and every wave's
+    read_ops(0, ops[0]);
+    // Iteration c: chunk c + 1 in LDS for every wave (its copies went out
+    // three iterations earlier; those of chunks c + 2 and c + 3 may be in
+    // flight), then the copies of chunk c + 4 into the stage of chunk c,
+    // whose operands every wave has read into registers (the reads were
+    // issued in the previous iteration and the barrier waits for them), then
+    // the reads of chunk c + 1 and the MFMAs of chunk c.  Two iterations per
+    // loop trip keep the register sets static.
+    auto iter = [&](int c, ChunkOps &cur, ChunkOps &nxt) __attribute__((always_inline)) {
+        wait_vmcnt<8 * (kRtStages - 2)>();
+        block_sync();
+        issue(min(c + kRtStages, nch - 1), c % kRtStages);
+        read_ops((c + 1) % kRtStages, nxt);  // past the last chunk: a stage that holds valid data
+        mfma_ops(cur);
+    };
+    int c = 0;
+    for (; c + 1 < nch; c += 2) {
+        iter(c, ops[0], ops[1]);
+        iter(c + 1, ops[1], ops[0]);
+    }
+    if (c < nch) iter(c, ops[0], ops[1]);
+    wait_vmcnt<0>();  // no copy into LDS outlives the loop
+    block_sync();     // ... for any wave, and every operand read is done: the stages are free
+
+    // The output tile goes out through LDS: each wave writes its 32 tokens x
+    // 64 experts there (fp32, rows padded to 68 floats so that the 16-byte
+    // writes of 16 lanes fall on distinct banks) and reads them back row by
+    // row, so that one store instruction writes 4 rows of 256 contiguous
+    // bytes.  Stored straight from the accumulators, each instruction would
+    // scatter 64 values of 4 bytes over 32 rows; those stores took about a
+    // third of the kernel at T = 4096 (and more at T = 32768).
+    constexpr int kOutRow = 68;
+    float *ot = reinterpret_cast<float *>(&wst[0][0]) + wave * 32 * kOutRow;
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4 *>(ot + n * kOutRow + 32 * v + 8 * g + 4 * h) =
+                make_float4(acc[v][4 * g], acc[v][4 * g + 1], acc[v][4 * g + 2], acc[v][4 * g + 3]);
+    // the rows are read back by the lanes of the same wave only
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const bool direct = a.KS == 1;
+    const int e0 = 64 * et + 4 * (lane & 15);  // this lane's 4 experts
+    float bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = (direct && a.bias && e0 + j < a.E) ? a.bias[e0 + j] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 4 * i + (lane >> 4);
+        const int t = tok0 + row;
+        if (t >= a.T) continue;
+        const float4 o = *reinterpret_cast<const float4 *>(ot + row * kOutRow + 4 * (lane & 15));
+        const float val[4] = {o.x + bv[0], o.y + bv[1], o.z + bv[2], o.w + bv[3]};
+        float *dst = a.out + ((size_t)ks * a.T + t) * a.E + e0;
+        if ((a.E & 3) == 0) {  // rows start 16-byte aligned: all 4 experts in range or none
+            if (e0 < a.E) *reinterpret_cast<float4 *>(dst) = make_float4(val[0], val[1], val[2], val[3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (e0 + j < a.E) dst[j] = val[j];
+        }
     }
 }
 
