@@ -37,6 +37,11 @@ SMALL = {
     # widths that are not multiples of 128 and odd K-step counts
     "T1000_E4_k2_pairs": (wl.Dims(T=1000, d=128, E=4, k=2, F=192, Fs=64, G=64), False),
     "T600_E2_k1_G128_pairs": (wl.Dims(T=600, d=256, E=2, k=1, F=128, Fs=128, G=128), False),
+    # expert counts that are not multiples of 4 (logit rows not 16-byte
+    # aligned: the router GEMM stores them value by value), with the router's
+    # K split into two ranges (d = 1024) and without (d = 256)
+    "T37_E30_d1024_ksplit": (wl.Dims(T=37, d=1024, E=30, k=4, F=64, Fs=64, G=64), False),
+    "T37_E13_k3": (wl.Dims(T=37, d=256, E=13, k=3, F=64, Fs=64, G=32), False),
 }
 
 
@@ -452,7 +457,7 @@ def _route_x(c, with_bias):
 
 ROUTER_CASES = [("c0_tiny", False), ("c1_decode", False), ("c2_prefill512", False),
                 ("c3_prefill4096_zipf", True), ("ragged_T37_E16_k4", False), ("T5_small_batch", True),
-                ("T8_k65_over_limit", False)]
+                ("T8_k65_over_limit", False), ("T37_E30_d1024_ksplit", True), ("T37_E13_k3", True)]
 
 
 @pytest.mark.parametrize("name,with_bias", ROUTER_CASES, ids=[n for n, _ in ROUTER_CASES])
