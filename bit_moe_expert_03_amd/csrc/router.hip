@@ -12,25 +12,27 @@
 // contiguous bytes; Epad = E rounded up to 64, padding rows zero.
 //
 // router_gemm_kernel: one block = 128 tokens x 64 experts over a K range,
-// each wave 32 tokens x the block's 64 experts (two 32-expert tiles).  Per
-// 64-wide K chunk the block's router rows (hi and lo, 64 experts, 16 KB) and
-// each wave's 32 activation rows (4 KB) are copied global -> LDS
-// (global_load_lds_dwordx4) into a ring of four stages, four chunks ahead of
-// the MFMAs that use them;
-// each router row is read from L2 once per 128 tokens.  v_mfma_f32_32x32x16
-// _bf16 with the router as the first operand, so lane l holds token l % 32 of
-// the wave's tile and register r of an expert tile holds expert 8 (r / 4) +
-// 4 (l / 32) + r % 4 of it.  When the grid would be small, K is split into
-// KS ranges whose partial logits a second kernel sums in range order
-// (deterministic), adding the bias; with KS = 1 the GEMM writes the logits
-// itself.
+// eight waves: wave w takes the 32 tokens of tile w % 4 against the block's
+// 64 experts (two 32-expert tiles) over half of every 64-wide K chunk (its
+// 16-wide sub-steps 2 (w / 4) and 2 (w / 4) + 1), so that two waves share
+// each SIMD and hide each other's barrier and LDS latency; the two halves'
+// sums are added at the end (half 0 + half 1).  Per K chunk the block's
+// router rows (hi and lo, 64 experts, 16 KB) and its 128 activation rows
+// (16 KB) are copied global -> LDS (global_load_lds_dwordx4) into a ring of
+// four stages, four chunks ahead of the MFMAs that use them; each router row
+// is read from L2 once per 128 tokens.  v_mfma_f32_32x32x16_bf16 with the
+// router as the first operand, so lane l holds token l % 32 of the wave's
+// tile and register r of an expert tile holds expert 8 (r / 4) + 4 (l / 32)
+// + r % 4 of it.  When the grid would be small, K is split into KS ranges
+// whose partial logits a second kernel sums in range order (deterministic),
+// adding the bias; with KS = 1 the GEMM writes the logits itself.
 #include <type_traits>
 
 #include "gemm_common.h"
 
 namespace moe {
 
-constexpr int kRouterThreads = 256;  // 4 waves per block
+constexpr int kRouterThreads = 512;  // 8 waves per block: 4 token tiles x 2 halves of each K chunk
 
 __global__ __launch_bounds__(256) void router_pack_kernel(const float *__restrict__ W, int d, int E, int Epad,
                                                           uint16_t *__restrict__ P)
@@ -61,40 +63,43 @@ struct RouterArgs {
 };
 
 // Router stage: [hi/lo][64 experts][8 chunks of 16 B], chunk kc of expert row
-// e at slot kc ^ ((e >> 1) & 7).  Activation stage of a wave: [32 tokens][8
-// chunks of 16 B], chunk kc of token row t at slot kc ^ ((t >> 1) & 7).  Both
-// keep the operand reads (32 rows x one chunk) free of bank conflicts.
+// e at slot kc ^ ((e >> 1) & 7).  Activation stage: [4 token tiles][32
+// tokens][8 chunks of 16 B], chunk kc of token row t at slot kc ^ ((t >> 1) &
+// 7).  Both keep the operand reads (32 rows x one chunk) free of bank
+// conflicts.
 constexpr int kRtWStage = 2 * 64 * 128;  // 16 KB
-constexpr int kRtXWave = 32 * 128;       // 4 KB
+constexpr int kRtXTile = 32 * 128;       // 4 KB
+constexpr int kOutRow = 68;              // floats per row of an output tile in LDS (64 + pad)
 
 __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs a)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t wst[kRtStages][kRtWStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t xst[kRtStages][4][kRtXWave];
+    __shared__ __attribute__((aligned(1024))) uint8_t xst[kRtStages][4][kRtXTile];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tw = wave & 3, kh = wave >> 2;  // token tile, half of each K chunk (sub-steps 2 kh, 2 kh + 1)
     const int per = a.ntb * a.net;
     const int ks = blockIdx.x / per;
     const int rem = blockIdx.x - ks * per;
     const int et = rem / a.ntb, tb = rem - et * a.ntb;
     const int n = lane & 31, h = lane >> 5;
-    // router copies: copy i of wave w fills the 16-byte positions 64 (4 i + w)
+    // router copies: copy i of wave w fills the 16-byte positions 64 (8 i + w)
     // + lane of a stage, i.e. (hi/lo, expert row, slot) = (p >> 9, (p >> 3) &
     // 63, p & 7); byte offsets from P at the block's first K column
-    uint32_t woff[4];
+    uint32_t woff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = 64 * (4 * i + wave) + lane;
+    for (int i = 0; i < 2; ++i) {
+        const int p = 64 * (8 * i + wave) + lane;
         const int hl = p >> 9, e = (p >> 3) & 63, kc = (p & 7) ^ ((e >> 1) & 7);
         woff[i] = (uint32_t)(((size_t)hl * a.Epad + 64 * et + e) * a.d * 2 + 16 * kc);
     }
-    // activation copies: copy j fills rows 8 j + lane / 8 of the wave's stage,
-    // slot lane & 7; rows past T load a valid row
-    uint32_t xoff[4];
-    int tok0 = kRtTok * tb + 32 * wave;
+    // activation copies: copy j of wave w fills rows 16 kh + 8 j + lane / 8 of
+    // token tile tw, slot lane & 7; rows past T load a valid row
+    uint32_t xoff[2];
+    const int tok0 = kRtTok * tb + 32 * tw;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = 8 * j + (lane >> 3);
+    for (int j = 0; j < 2; ++j) {
+        const int row = 16 * kh + 8 * j + (lane >> 3);
         const int kc = (lane & 7) ^ ((row >> 1) & 7);
         xoff[j] = (uint32_t)min(tok0 + row, a.T - 1) * (uint32_t)a.d * 2u + 16u * (uint32_t)kc;
     }
@@ -102,9 +107,9 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
     auto issue = [&](int c, int stage) __attribute__((always_inline)) {
         const uint16_t *wb = a.P + k0 + c * kRtK, *xb = a.x + k0 + c * kRtK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(wb, woff[i], &wst[stage][(4 * i + wave) * 1024]);
+        for (int i = 0; i < 2; ++i) dma16(wb, woff[i], &wst[stage][(8 * i + wave) * 1024]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(xb, xoff[j], &xst[stage][wave][j * 1024]);
+        for (int j = 0; j < 2; ++j) dma16(xb, xoff[j], &xst[stage][tw][(2 * kh + j) * 1024]);
     };
     f32x16 acc[2];
 #pragma unroll
@@ -112,37 +117,34 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[v][r] = 0.f;
 
-    // The operands of one chunk (per 16-wide sub-step q: the activation
-    // chunk 2 q + h of token n, router chunks of experts n and 32 + n, hi
-    // and lo) are read from LDS into registers one chunk ahead, so that the
-    // reads of chunk c + 1 are in flight under the MFMAs of chunk c: with
-    // one wave per SIMD nothing else hides the LDS latency of an operand
-    // read right before its MFMA.
+    // The operands of this wave's half of a chunk (per 16-wide sub-step q:
+    // the activation chunk 2 q + h of token n, router chunks of experts n and
+    // 32 + n, hi and lo) are read from LDS into registers one chunk ahead.
     struct ChunkOps {
-        bf16x8 x[4], w[4][2][2];  // [sub-step][expert tile][hi, lo]
+        bf16x8 x[2], w[2][2][2];  // [sub-step][expert tile][hi, lo]
     };
     auto read_ops = [&](int stage, ChunkOps &o) __attribute__((always_inline)) {
-        const uint8_t *ws = wst[stage], *xs = xst[stage][wave];
+        const uint8_t *ws = wst[stage], *xs = xst[stage][tw];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int kc = 2 * q + h;
-            o.x[q] = *reinterpret_cast<const bf16x8 *>(xs + n * 128 + 16 * (kc ^ ((n >> 1) & 7)));
+        for (int qq = 0; qq < 2; ++qq) {
+            const int kc = 2 * (2 * kh + qq) + h;
+            o.x[qq] = *reinterpret_cast<const bf16x8 *>(xs + n * 128 + 16 * (kc ^ ((n >> 1) & 7)));
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
                 const int e = 32 * v + n;
                 const int off = e * 128 + 16 * (kc ^ ((e >> 1) & 7));
-                o.w[q][v][0] = *reinterpret_cast<const bf16x8 *>(ws + off);
-                o.w[q][v][1] = *reinterpret_cast<const bf16x8 *>(ws + 64 * 128 + off);
+                o.w[qq][v][0] = *reinterpret_cast<const bf16x8 *>(ws + off);
+                o.w[qq][v][1] = *reinterpret_cast<const bf16x8 *>(ws + 64 * 128 + off);
             }
         }
     };
     auto mfma_ops = [&](const ChunkOps &o) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
-                acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[q][v][0], o.x[q], acc[v], 0, 0, 0);
-                acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[q][v][1], o.x[q], acc[v], 0, 0, 0);
+                acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[qq][v][0], o.x[qq], acc[v], 0, 0, 0);
+                acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[qq][v][1], o.x[qq], acc[v], 0, 0, 0);
             }
     };
 
@@ -152,18 +154,16 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
 #pragma unroll
     for (int c = 0; c < kRtStages; ++c) issue(min(c, nch - 1), c);
     ChunkOps ops[2];
-    wait_vmcnt<8 * (kRtStages - 1)>();  // this wave's copies of chunk 0 have landed
+    wait_vmcnt<4 * (kRtStages - 1)>();  // this wave's copies of chunk 0 have landed
     block_sync();                         // ... and every wave's
     read_ops(0, ops[0]);
     // Iteration c: chunk c + 1 in LDS for every wave (its copies went out
     // three iterations earlier; those of chunks c + 2 and c + 3 may be in
     // flight), then the copies of chunk c + 4 into the stage of chunk c,
-    // whose operands every wave has read into registers (the reads were
-    // issued in the previous iteration and the barrier waits for them), then
-    // the reads of chunk c + 1 and the MFMAs of chunk c.  Two iterations per
-    // loop trip keep the register sets static.
+    // whose operands every wave has read into registers, then the reads of
+    // chunk c + 1 and the MFMAs of chunk c.
     auto iter = [&](int c, ChunkOps &cur, ChunkOps &nxt) __attribute__((always_inline)) {
-        wait_vmcnt<8 * (kRtStages - 2)>();
+        wait_vmcnt<4 * (kRtStages - 2)>();
         block_sync();
         issue(min(c + kRtStages, nch - 1), c % kRtStages);
         read_ops((c + 1) % kRtStages, nxt);  // past the last chunk: a stage that holds valid data
@@ -178,35 +178,34 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
     wait_vmcnt<0>();  // no copy into LDS outlives the loop
     block_sync();     // ... for any wave, and every operand read is done: the stages are free
 
-    // The output tile goes out through LDS: each wave writes its 32 tokens x
-    // 64 experts there (fp32, rows padded to 68 floats so that the 16-byte
-    // writes of 16 lanes fall on distinct banks) and reads them back row by
-    // row, so that one store instruction writes 4 rows of 256 contiguous
-    // bytes.  Stored straight from the accumulators, each instruction would
-    // scatter 64 values of 4 bytes over 32 rows; those stores took about a
-    // third of the kernel at T = 4096 (and more at T = 32768).
-    constexpr int kOutRow = 68;
-    float *ot = reinterpret_cast<float *>(&wst[0][0]) + wave * 32 * kOutRow;
+    // The two K halves of each token tile go to LDS as row-major tiles (rows
+    // padded to 68 floats, so that the 16-byte writes of 16 lanes fall on
+    // distinct banks): half 0 in the router stages, half 1 in the activation
+    // stages.  Then every wave sums 16 rows of one tile (half 0 + half 1, in
+    // that order) and stores them as whole 256-byte row segments.
+    float *ot = reinterpret_cast<float *>(kh == 0 ? &wst[0][0] : &xst[0][0][0]) + tw * 32 * kOutRow;
 #pragma unroll
     for (int v = 0; v < 2; ++v)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             *reinterpret_cast<float4 *>(ot + n * kOutRow + 32 * v + 8 * g + 4 * h) =
                 make_float4(acc[v][4 * g], acc[v][4 * g + 1], acc[v][4 * g + 2], acc[v][4 * g + 3]);
-    // the rows are read back by the lanes of the same wave only
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_sync();
+    const float *t0 = reinterpret_cast<const float *>(&wst[0][0]) + tw * 32 * kOutRow;
+    const float *t1 = reinterpret_cast<const float *>(&xst[0][0][0]) + tw * 32 * kOutRow;
     const bool direct = a.KS == 1;
     const int e0 = 64 * et + 4 * (lane & 15);  // this lane's 4 experts
     float bv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bv[j] = (direct && a.bias && e0 + j < a.E) ? a.bias[e0 + j] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 4 * i + (lane >> 4);
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * kh + 4 * i + (lane >> 4);
         const int t = tok0 + row;
         if (t >= a.T) continue;
-        const float4 o = *reinterpret_cast<const float4 *>(ot + row * kOutRow + 4 * (lane & 15));
-        const float val[4] = {o.x + bv[0], o.y + bv[1], o.z + bv[2], o.w + bv[3]};
+        const float4 o0 = *reinterpret_cast<const float4 *>(t0 + row * kOutRow + 4 * (lane & 15));
+        const float4 o1 = *reinterpret_cast<const float4 *>(t1 + row * kOutRow + 4 * (lane & 15));
+        const float val[4] = {o0.x + o1.x + bv[0], o0.y + o1.y + bv[1], o0.z + o1.z + bv[2], o0.w + o1.w + bv[3]};
         float *dst = a.out + ((size_t)ks * a.T + t) * a.E + e0;
         if ((a.E & 3) == 0) {  // rows start 16-byte aligned: all 4 experts in range or none
             if (e0 < a.E) *reinterpret_cast<float4 *>(dst) = make_float4(val[0], val[1], val[2], val[3]);
@@ -233,14 +232,17 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float *__restr
 
 int router_epad(int E) { return (E + 63) & ~63; }
 
-// K ranges: split until the grid has a block per compute unit (256), each
-// range a whole number of K chunks and at least kRtMinChunks of them
+// K ranges: split until the grid has a block for every other compute unit
+// (128 blocks of 8 waves), each range a whole number of K chunks and at
+// least kRtMinChunks of them.  Measured at T = 4096 (128 blocks): no split,
+// route from x 31.0-31.5 us, against 33.0-33.4 us with two K ranges (256
+// blocks) and their partial sum.
 int router_splits(int T, int d, int E)
 {
     const int64_t blocks = (int64_t)((T + kRtTok - 1) / kRtTok) * (router_epad(E) / 64);
     const int nch = d / kRtK;
     int ks = 1;
-    while (blocks * ks < 256 && nch % (ks * 2) == 0 && nch / (ks * 2) >= kRtMinChunks) ks *= 2;
+    while (blocks * ks < 128 && nch % (ks * 2) == 0 && nch / (ks * 2) >= kRtMinChunks) ks *= 2;
     return ks;
 }
 
