@@ -11,16 +11,17 @@
 // rows, then lo rows), expert-major so that each lane's MFMA operand is 16
 // contiguous bytes; Epad = E rounded up to 64, padding rows zero.
 //
-// router_gemm_kernel: one block = 128 tokens x 64 experts over a K range,
-// eight waves: wave w takes the 32 tokens of tile w % 4 against the block's
-// 64 experts (two 32-expert tiles) over half of every 64-wide K chunk (its
-// 16-wide sub-steps 2 (w / 4) and 2 (w / 4) + 1), so that two waves share
-// each SIMD and hide each other's barrier and LDS latency; the two halves'
-// sums are added at the end (half 0 + half 1).  Per K chunk the block's
-// router rows (hi and lo, 64 experts, 16 KB) and its 128 activation rows
-// (16 KB) are copied global -> LDS (global_load_lds_dwordx4) into a ring of
-// four stages, four chunks ahead of the MFMAs that use them; each router row
-// is read from L2 once per 128 tokens.  v_mfma_f32_32x32x16_bf16 with the
+// router_gemm_kernel: one block = 128 tokens x EX experts (64, or 32 for
+// batches that would not fill the chip) over a K range, eight waves: wave w
+// takes the 32 tokens of tile w % 4 against the block's experts (EX / 32
+// tiles of 32) over half of every 64-wide K chunk (its 16-wide sub-steps
+// 2 (w / 4) and 2 (w / 4) + 1), so that two waves share each SIMD and hide
+// each other's barrier and LDS latency; the two halves' sums are added at
+// the end (half 0 + half 1).  Per K chunk the block's router rows (hi and
+// lo, EX experts) and its 128 activation rows (16 KB) are copied global ->
+// LDS (global_load_lds_dwordx4) into a ring of four stages, four chunks
+// ahead of the MFMAs that use them; each router row is read from L2 once per
+// 128 tokens.  v_mfma_f32_32x32x16_bf16 with the
 // router as the first operand, so lane l holds token l % 32 of the wave's
 // tile and register r of an expert tile holds expert 8 (r / 4) + 4 (l / 32)
 // + r % 4 of it.  When the grid would be small, K is split into KS ranges
@@ -59,21 +60,27 @@ struct RouterArgs {
     const float *bias;    // [E] or null
     float *out;           // KS == 1: logits [T][E]; else partials [KS][T][E]
     int T, d, E, Epad, KS, kper;
-    int ntb, net;         // token blocks (128), expert tiles (64)
+    int ntb, net;         // token blocks (128), expert tiles (EX experts each)
 };
 
-// Router stage: [hi/lo][64 experts][8 chunks of 16 B], chunk kc of expert row
-// e at slot kc ^ ((e >> 1) & 7).  Activation stage: [4 token tiles][32
+// Router stage: [hi/lo][EX experts][8 chunks of 16 B], chunk kc of expert
+// row e at slot kc ^ ((e >> 1) & 7).  Activation stage: [4 token tiles][32
 // tokens][8 chunks of 16 B], chunk kc of token row t at slot kc ^ ((t >> 1) &
 // 7).  Both keep the operand reads (32 rows x one chunk) free of bank
 // conflicts.
-constexpr int kRtWStage = 2 * 64 * 128;  // 16 KB
 constexpr int kRtXTile = 32 * 128;       // 4 KB
-constexpr int kOutRow = 68;              // floats per row of an output tile in LDS (64 + pad)
 
+// EX = 64 or 32 experts per block (NT = EX / 32 expert tiles per wave).
+// With 32, a batch gets twice the blocks for the same work, each re-reading
+// the activations once per 32 experts instead of once per 64.
+template <int EX>
 __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t wst[kRtStages][kRtWStage];
+    constexpr int NT = EX / 32;
+    constexpr int kCopies = NT + 2;        // global->LDS copies per wave and K chunk (router, activations)
+    constexpr int kWStage = 2 * EX * 128;  // hi and lo rows of the block's experts, one K chunk
+    constexpr int kOutRow = EX + 4;        // floats per row of an output tile in LDS (padded)
+    __shared__ __attribute__((aligned(1024))) uint8_t wst[kRtStages][kWStage];
     __shared__ __attribute__((aligned(1024))) uint8_t xst[kRtStages][4][kRtXTile];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -84,14 +91,14 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
     const int et = rem / a.ntb, tb = rem - et * a.ntb;
     const int n = lane & 31, h = lane >> 5;
     // router copies: copy i of wave w fills the 16-byte positions 64 (8 i + w)
-    // + lane of a stage, i.e. (hi/lo, expert row, slot) = (p >> 9, (p >> 3) &
-    // 63, p & 7); byte offsets from P at the block's first K column
-    uint32_t woff[2];
+    // + lane of a stage, i.e. (hi/lo, expert row, slot) = (p / (8 EX),
+    // (p >> 3) % EX, p & 7); byte offsets from P at the block's first K column
+    uint32_t woff[NT];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NT; ++i) {
         const int p = 64 * (8 * i + wave) + lane;
-        const int hl = p >> 9, e = (p >> 3) & 63, kc = (p & 7) ^ ((e >> 1) & 7);
-        woff[i] = (uint32_t)(((size_t)hl * a.Epad + 64 * et + e) * a.d * 2 + 16 * kc);
+        const int hl = p / (8 * EX), e = (p >> 3) & (EX - 1), kc = (p & 7) ^ ((e >> 1) & 7);
+        woff[i] = (uint32_t)(((size_t)hl * a.Epad + EX * et + e) * a.d * 2 + 16 * kc);
     }
     // activation copies: copy j of wave w fills rows 16 kh + 8 j + lane / 8 of
     // token tile tw, slot lane & 7; rows past T load a valid row
@@ -107,21 +114,21 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
     auto issue = [&](int c, int stage) __attribute__((always_inline)) {
         const uint16_t *wb = a.P + k0 + c * kRtK, *xb = a.x + k0 + c * kRtK;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) dma16(wb, woff[i], &wst[stage][(8 * i + wave) * 1024]);
+        for (int i = 0; i < NT; ++i) dma16(wb, woff[i], &wst[stage][(8 * i + wave) * 1024]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) dma16(xb, xoff[j], &xst[stage][tw][(2 * kh + j) * 1024]);
     };
-    f32x16 acc[2];
+    f32x16 acc[NT];
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
+    for (int v = 0; v < NT; ++v)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[v][r] = 0.f;
 
     // The operands of this wave's half of a chunk (per 16-wide sub-step q:
-    // the activation chunk 2 q + h of token n, router chunks of experts n and
-    // 32 + n, hi and lo) are read from LDS into registers one chunk ahead.
+    // the activation chunk 2 q + h of token n, router chunks of experts
+    // 32 v + n, hi and lo) are read from LDS into registers one chunk ahead.
     struct ChunkOps {
-        bf16x8 x[2], w[2][2][2];  // [sub-step][expert tile][hi, lo]
+        bf16x8 x[2], w[2][NT][2];  // [sub-step][expert tile][hi, lo]
     };
     auto read_ops = [&](int stage, ChunkOps &o) __attribute__((always_inline)) {
         const uint8_t *ws = wst[stage], *xs = xst[stage][tw];
@@ -130,11 +137,11 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
             const int kc = 2 * (2 * kh + qq) + h;
             o.x[qq] = *reinterpret_cast<const bf16x8 *>(xs + n * 128 + 16 * (kc ^ ((n >> 1) & 7)));
 #pragma unroll
-            for (int v = 0; v < 2; ++v) {
+            for (int v = 0; v < NT; ++v) {
                 const int e = 32 * v + n;
                 const int off = e * 128 + 16 * (kc ^ ((e >> 1) & 7));
                 o.w[qq][v][0] = *reinterpret_cast<const bf16x8 *>(ws + off);
-                o.w[qq][v][1] = *reinterpret_cast<const bf16x8 *>(ws + 64 * 128 + off);
+                o.w[qq][v][1] = *reinterpret_cast<const bf16x8 *>(ws + EX * 128 + off);
             }
         }
     };
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-            for (int v = 0; v < 2; ++v) {
+            for (int v = 0; v < NT; ++v) {
                 acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[qq][v][0], o.x[qq], acc[v], 0, 0, 0);
                 acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[qq][v][1], o.x[qq], acc[v], 0, 0, 0);
             }
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
 #pragma unroll
     for (int c = 0; c < kRtStages; ++c) issue(min(c, nch - 1), c);
     ChunkOps ops[2];
-    wait_vmcnt<4 * (kRtStages - 1)>();  // this wave's copies of chunk 0 have landed
+    wait_vmcnt<kCopies * (kRtStages - 1)>();  // this wave's copies of chunk 0 have landed
     block_sync();                         // ... and every wave's
     read_ops(0, ops[0]);
     // Iteration c: chunk c + 1 in LDS for every wave (its copies went out
@@ -163,7 +170,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
     // whose operands every wave has read into registers, then the reads of
     // chunk c + 1 and the MFMAs of chunk c.
     auto iter = [&](int c, ChunkOps &cur, ChunkOps &nxt) __attribute__((always_inline)) {
-        wait_vmcnt<4 * (kRtStages - 2)>();
+        wait_vmcnt<kCopies * (kRtStages - 2)>();
         block_sync();
         issue(min(c + kRtStages, nch - 1), c % kRtStages);
         read_ops((c + 1) % kRtStages, nxt);  // past the last chunk: a stage that holds valid data
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
     // that order) and stores them as whole 256-byte row segments.
     float *ot = reinterpret_cast<float *>(kh == 0 ? &wst[0][0] : &xst[0][0][0]) + tw * 32 * kOutRow;
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
+    for (int v = 0; v < NT; ++v)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             *reinterpret_cast<float4 *>(ot + n * kOutRow + 32 * v + 8 * g + 4 * h) =
@@ -194,17 +201,18 @@ __global__ __launch_bounds__(kRouterThreads) void router_gemm_kernel(RouterArgs 
     const float *t0 = reinterpret_cast<const float *>(&wst[0][0]) + tw * 32 * kOutRow;
     const float *t1 = reinterpret_cast<const float *>(&xst[0][0][0]) + tw * 32 * kOutRow;
     const bool direct = a.KS == 1;
-    const int e0 = 64 * et + 4 * (lane & 15);  // this lane's 4 experts
+    constexpr int LPR = EX / 4;  // lanes per output row (4 experts each)
+    const int e0 = EX * et + 4 * (lane & (LPR - 1));  // this lane's 4 experts
     float bv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bv[j] = (direct && a.bias && e0 + j < a.E) ? a.bias[e0 + j] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 16 * kh + 4 * i + (lane >> 4);
+    for (int i = 0; i < 16 * LPR / 64; ++i) {
+        const int row = 16 * kh + (64 / LPR) * i + lane / LPR;
         const int t = tok0 + row;
         if (t >= a.T) continue;
-        const float4 o0 = *reinterpret_cast<const float4 *>(t0 + row * kOutRow + 4 * (lane & 15));
-        const float4 o1 = *reinterpret_cast<const float4 *>(t1 + row * kOutRow + 4 * (lane & 15));
+        const float4 o0 = *reinterpret_cast<const float4 *>(t0 + row * kOutRow + 4 * (lane & (LPR - 1)));
+        const float4 o1 = *reinterpret_cast<const float4 *>(t1 + row * kOutRow + 4 * (lane & (LPR - 1)));
         const float val[4] = {o0.x + o1.x + bv[0], o0.y + o1.y + bv[1], o0.z + o1.z + bv[2], o0.w + o1.w + bv[3]};
         float *dst = a.out + ((size_t)ks * a.T + t) * a.E + e0;
         if ((a.E & 3) == 0) {  // rows start 16-byte aligned: all 4 experts in range or none
@@ -232,14 +240,24 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float *__restr
 
 int router_epad(int E) { return (E + 63) & ~63; }
 
+// Experts per block: 32 where blocks of 64 would give fewer blocks than
+// compute units.  Measured at T = 4096 (256 blocks of 32 against 128 of 64):
+// route from x 27.7-28.5 us against 30.8-31.0 us; T = 512: 22.5 against
+// 24.2-25.5 us.  At T = 32768 blocks of 32 were slower (the activations are
+// read once per 32 experts instead of once per 64).
+static int router_ex(int T, int E)
+{
+    return (int64_t)((T + kRtTok - 1) / kRtTok) * (router_epad(E) / 64) < 256 ? 32 : 64;
+}
+
 // K ranges: split until the grid has a block for every other compute unit
 // (128 blocks of 8 waves), each range a whole number of K chunks and at
-// least kRtMinChunks of them.  Measured at T = 4096 (128 blocks): no split,
-// route from x 31.0-31.5 us, against 33.0-33.4 us with two K ranges (256
-// blocks) and their partial sum.
+// least kRtMinChunks of them.  Measured at T = 4096 with 64 experts per
+// block (128 blocks): no split, route from x 31.0-31.5 us, against
+// 33.0-33.4 us with two K ranges (256 blocks) and their partial sum.
 int router_splits(int T, int d, int E)
 {
-    const int64_t blocks = (int64_t)((T + kRtTok - 1) / kRtTok) * (router_epad(E) / 64);
+    const int64_t blocks = (int64_t)((T + kRtTok - 1) / kRtTok) * (router_epad(E) / router_ex(T, E));
     const int nch = d / kRtK;
     int ks = 1;
     while (blocks * ks < 128 && nch % (ks * 2) == 0 && nch / (ks * 2) >= kRtMinChunks) ks *= 2;
@@ -265,11 +283,15 @@ hipError_t launch_router(const Plan &p, const uint16_t *x, const uint16_t *P, co
     a.KS = router_splits(p.T, p.d, p.E);
     a.kper = p.d / a.KS;
     a.ntb = (p.T + kRtTok - 1) / kRtTok;
-    a.net = a.Epad / 64;
+    const int ex = router_ex(p.T, p.E);
+    a.net = a.Epad / ex;
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_router);
     a.out = a.KS == 1 ? logits : part;
     const int64_t blocks = (int64_t)a.ntb * a.net * a.KS;
-    hipLaunchKernelGGL(router_gemm_kernel, dim3((unsigned)blocks), dim3(kRouterThreads), 0, s, a);
+    if (ex == 32)
+        hipLaunchKernelGGL(router_gemm_kernel<32>, dim3((unsigned)blocks), dim3(kRouterThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(router_gemm_kernel<64>, dim3((unsigned)blocks), dim3(kRouterThreads), 0, s, a);
     if (a.KS > 1) {
         const int64_t TE = (int64_t)p.T * p.E;
         hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((TE + 255) / 256)), dim3(256), 0, s,
