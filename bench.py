@@ -172,7 +172,7 @@ class CacheFlush:
         self.dst.copy_(self.src)
 
 
-def run_timed(B, dm, calls, steps, warmup, flush=None):
+def run_timed(B, dm, calls, steps, warmup, flush=None, queue_ahead=False):
     """calls[i] = (logits, x, weights_struct, y) for step i % len(calls).
 
     Timed region: one HIP graph of `steps` consecutive layer calls, replayed
@@ -181,7 +181,8 @@ def run_timed(B, dm, calls, steps, warmup, flush=None):
     each replay, outside the timed region.  Per-kernel times: right after,
     the same `steps` calls eagerly through moe_layer_timed, whose kernels are
     launched with start/stop events (hipExtLaunchKernel) on the launch
-    stream.  Returns (seconds, mean ms per kernel)."""
+    stream (with `queue_ahead`, behind a spin kernel, so that they run back
+    to back).  Returns (seconds, mean ms per kernel)."""
     import torch
     nk = B.moe_layer_kernels(dm)
     r = B.alloc_routing(dm)
@@ -216,6 +217,13 @@ def run_timed(B, dm, calls, steps, warmup, flush=None):
         flush()
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
+        if queue_ahead:
+            # a spin kernel first (about 0.1 s of shader clocks), so that the
+            # eager launches queue up behind it and then run back to back as
+            # in the graph, instead of one by one as the host submits them
+            # (a decode layer's two kernels take less GPU time than the host
+            # takes to submit them with their events)
+            torch.cuda._sleep(200_000_000)
         for i in range(steps):
             lg, x, w, y = calls[i % len(calls)]
             B.moe_layer_timed(dm, lg, x, w, r, y, ws, [e.cuda_event for e in evs[i]], stream=stream)
@@ -249,7 +257,7 @@ def bench_decode(B, wl, args):
         host_inputs.append(c)
     log("decode: capturing and timing")
     flush = CacheFlush()
-    sec, per_kernel = run_timed(B, dm, calls, args.steps, args.warmup, flush)
+    sec, per_kernel = run_timed(B, dm, calls, args.steps, args.warmup, flush, queue_ahead=True)
     value = args.steps / sec
     names, kernel = ["decode_gateup", "decode_down"], "decode_gateup_kernel"
     dom_bytes = gateup_decode_bytes(dims)
@@ -292,7 +300,7 @@ def bench_small_batches(B, wl, args, dims, seed, sets):
             c = wl.make_case(dT, seed=seed, index=1000 + 40 * T + s, weights=False)
             y = torch.empty((T, dims.d), dtype=torch.int16, device="cuda")
             calls.append((to_dev(c["logits"]), to_dev(c["x"]), sets[s][1], y))
-        sec, per_kernel = run_timed(B, dm, calls, steps, 8)
+        sec, per_kernel = run_timed(B, dm, calls, steps, 8, queue_ahead=True)
         out[f"T{T}"] = {"tokens_per_s": T * steps / sec, "us_per_step": sec * 1e6 / steps,
                         "per_kernel_us": [k * 1e3 for k in per_kernel]}
         log(f"small batch T={T}: {sec * 1e6 / steps:.1f} us/step, {T * steps / sec:.0f} tok/s")
