@@ -56,7 +56,6 @@ constexpr int kGemmThreads = 256;      // 4 waves
 // conflicts.
 // B buffers (2, one per pair of K steps): [4 waves][64 rows][64 bytes] of raw
 // 4-bit codes; chunk c of row r at slot c ^ ((r >> 2) & 3).
-constexpr int kMaxMS = 4;
 constexpr int kARow = 128;                        // bytes per A row in LDS
 constexpr int kBRow = 64;                         // bytes of codes per B row per pair of K steps
 constexpr int kBWave = 64 * kBRow;                // 4 KB per wave

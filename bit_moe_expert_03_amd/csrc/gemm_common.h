@@ -179,19 +179,6 @@ __device__ __forceinline__ void store_row32(uint16_t *rowp, const float (&v)[16]
         *reinterpret_cast<uint4 *>(rowp + 16 * p + 8 * h) = make_uint4(d[2 * p][0], d[2 * p][1], d[2 * p + 1][0], d[2 * p + 1][1]);
 }
 
-// scheduling hint: interleave n MFMAs with the decode VALU and LDS reads of
-// the next sub-step (6 VALU ops fit under one 32x32x16 MFMA)
-template <int NMFMA, int NDS>
-__device__ __forceinline__ void interleave_hint()
-{
-#pragma unroll
-    for (int i = 0; i < NMFMA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
-    }
-}
-
 // scheduling hint for a sub-step of MS pairs of MFMAs: each pair (the two
 // MFMAs that read one A operand) is followed by NDS LDS reads (the operand's
 // reload for the next sub-step) and 12 VALU ops (decode of the next sub-step)

@@ -20,24 +20,6 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
     return __uint_as_float(bits16 << 16);
 }
 
-// byte I of v as fp32: one v_cvt_f32_ubyte{I}.  Written as inline asm so the
-// compiler cannot turn "byte I of a nibble-masked word" into a bit-field
-// extract followed by a byte-0 conversion (two instructions).
-template <int I>
-__device__ __forceinline__ float ubyte_f32(uint32_t v)
-{
-    float r;
-    if constexpr (I == 0)
-        __asm__("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
-    else if constexpr (I == 1)
-        __asm__("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
-    else if constexpr (I == 2)
-        __asm__("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
-    else
-        __asm__("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
-    return r;
-}
-
 // two fp32 -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32);
 // `lo` lands in bits 0..15
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
@@ -76,22 +58,6 @@ __device__ __forceinline__ void dequant8_bf16(uint32_t v, float s, float b, uint
     out[1] = pack_bf16x2(__builtin_fmaf(s9, l01[1], b), __builtin_fmaf(s9, h01[1], b));
     out[2] = pack_bf16x2(__builtin_fmaf(s9, l23[0], b), __builtin_fmaf(s9, h23[0], b));
     out[3] = pack_bf16x2(__builtin_fmaf(s9, l23[1], b), __builtin_fmaf(s9, h23[1], b));
-}
-
-// sum_i q_i * x_i over the 8 codes of one dword (x in element order)
-__device__ __forceinline__ float dot8_codes(uint32_t v, const float *x, float acc)
-{
-    const uint32_t lo = v & 0x0F0F0F0Fu;
-    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
-    acc = __builtin_fmaf(ubyte_f32<0>(lo), x[0], acc);
-    acc = __builtin_fmaf(ubyte_f32<0>(hi), x[1], acc);
-    acc = __builtin_fmaf(ubyte_f32<1>(lo), x[2], acc);
-    acc = __builtin_fmaf(ubyte_f32<1>(hi), x[3], acc);
-    acc = __builtin_fmaf(ubyte_f32<2>(lo), x[4], acc);
-    acc = __builtin_fmaf(ubyte_f32<2>(hi), x[5], acc);
-    acc = __builtin_fmaf(ubyte_f32<3>(lo), x[6], acc);
-    acc = __builtin_fmaf(ubyte_f32<3>(hi), x[7], acc);
-    return acc;
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
