@@ -163,3 +163,37 @@ def make_case(name_or_dims, seed: Optional[int] = None, index: int = 0,
         case["w"] = make_weights(dims, seed, index)
     return case
 
+
+
+# ---- decode attention over grouped KV heads (the pages' second decode workload)
+
+@dataclasses.dataclass(frozen=True)
+class AttnDims:
+    """One decode token: Hq query heads, Hkv KV heads (Hq = 8 Hkv: eight query
+    heads share one KV head), head dimension D, L cached tokens."""
+
+    Hq: int
+    Hkv: int
+    D: int
+    L: int
+
+
+# The pages name the sharing (8 query heads per KV head) and the contexts
+# (4K in their benchmarks, 32K for the packing figure, up to 128K); the head
+# counts and dimension below are this library's choice.
+ATTN_CONFIGS: Dict[str, AttnDims] = {
+    "attn_L4096": AttnDims(Hq=32, Hkv=4, D=128, L=4096),
+    "attn_L32768": AttnDims(Hq=32, Hkv=4, D=128, L=32768),
+    "attn_L131072": AttnDims(Hq=32, Hkv=4, D=128, L=131072),
+}
+_ATTN_TID = {"q": 20, "k": 21, "v": 22}
+
+
+def make_attn_case(name_or_dims, seed: int = 7, index: int = 0) -> dict:
+    """q [Hq][D] and the K, V caches [Hkv][L][D]: N(0, 1) rounded to bf16."""
+    dims = ATTN_CONFIGS[name_or_dims] if isinstance(name_or_dims, str) else name_or_dims
+    out = {"dims": dims, "seed": seed}
+    shapes = {"q": (dims.Hq, dims.D), "k": (dims.Hkv, dims.L, dims.D), "v": (dims.Hkv, dims.L, dims.D)}
+    for name, shape in shapes.items():
+        out[name] = to_bf16_bits(_rng(seed, index, _ATTN_TID[name]).standard_normal(shape, dtype=np.float32))
+    return out

@@ -63,6 +63,8 @@ def _declare(lib):
     lib.oracle_ffn.argtypes = [ctypes.c_int] * 7 + [_U16P, ctypes.POINTER(_OWeights), _U16P, _I32P, _F64P,
                                                     _I32P, ctypes.c_int, _F64P]
     lib.oracle_router_logits.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _U16P, _F32P, _F32P, _F64P]
+    lib.oracle_gqa_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _U16P, _U16P, _U16P,
+                                      _F64P]
     return lib
 
 
@@ -169,6 +171,21 @@ def router_logits(x_bits: np.ndarray, w_router: np.ndarray, bias: Optional[np.nd
     b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     lib.oracle_router_logits(T, d, E, _p(x, _U16P), _p(W, _F32P), None if b is None else _p(b, _F32P), _p(L, _F64P))
     return L
+
+
+def gqa_decode(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, lib=None) -> np.ndarray:
+    """fp64 decode attention of one token: q bf16 bits [Hq][D], k and v bf16
+    bits [Hkv][L][D]; query head h reads KV head h // (Hq // Hkv)."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    k = np.ascontiguousarray(k_bits, dtype=np.uint16)
+    v = np.ascontiguousarray(v_bits, dtype=np.uint16)
+    Hq, D = q.shape
+    Hkv, L, D2 = k.shape
+    assert D2 == D and v.shape == k.shape and Hq % Hkv == 0
+    out = np.empty((Hq, D), np.float64)
+    lib.oracle_gqa_decode(Hq, Hkv, D, L, _p(q, _U16P), _p(k, _U16P), _p(v, _U16P), _p(out, _F64P))
+    return out
 
 
 def ffn(dims, x_bits: np.ndarray, weights: dict, ids: np.ndarray, w: np.ndarray,

@@ -23,7 +23,10 @@
  *  - the router scores each token against every expert: logits = x W_r
  *    (+ a per-expert bias), W_r fp32 [d][E] (the step before the routing on
  *    the same page, section "What Lily actually does": each token's router
- *    picks its experts).
+ *    picks its experts);
+ *  - a second workload, decode attention of one token over grouped KV heads
+ *    (eight query heads share one KV head: same page, section "Decode
+ *    optimizations"), as scaled dot-product attention (oracle_gqa_decode).
  *
  * Readings of what the pages leave open (each is pinned by a CPU test):
  *  - top-k order: larger logit first, ties to the lower expert id, -0 == +0;
@@ -284,4 +287,45 @@ void oracle_router_logits(int T, int d, int E, const uint16_t *x, const float *W
             if (bias) acc += (double)bias[e];
             L[(size_t)t * E + e] = acc;
         }
+}
+
+/* Decode attention of one token over grouped KV heads (a second workload of
+ * the pages: page "Perplexity's Lily Beats MLX-LM by 1.35x Running Qwen3.6 on
+ * Apple Silicon", section "Decode optimizations": eight query heads share one
+ * KV head; the model's full-attention layers: page "Perplexity Open Sources
+ * Lily Inference Engine for Apple Silicon", opening paragraphs).  The pages do
+ * not write the formula; this is scaled dot-product attention.  Query head h
+ * reads KV head g = h / (Hq / Hkv):
+ *   s_t = (q_h . k_{g,t}) / sqrt(D),  p_t = exp(s_t - max s) / sum_u exp(s_u - max s),
+ *   o_h = sum_t p_t v_{g,t},
+ * in fp64 from bf16 inputs: q [Hq][D], k and v [Hkv][L][D] (token rows),
+ * out [Hq][D]. */
+void oracle_gqa_decode(int Hq, int Hkv, int D, int L, const uint16_t *q, const uint16_t *k,
+                       const uint16_t *v, double *out)
+{
+    const int G = Hq / Hkv;
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < Hq; ++h) {
+        const int g = h / G;
+        double *s = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        double smax = -INFINITY;
+        for (int t = 0; t < L; ++t) {
+            double acc = 0.0;
+            for (int i = 0; i < D; ++i)
+                acc += bf16_value(q[(size_t)h * D + i]) * bf16_value(k[((size_t)g * L + t) * D + i]);
+            s[t] = acc / sqrt((double)D);
+            if (s[t] > smax) smax = s[t];
+        }
+        double den = 0.0;
+        for (int t = 0; t < L; ++t) {
+            s[t] = exp(s[t] - smax);
+            den += s[t];
+        }
+        for (int i = 0; i < D; ++i) {
+            double acc = 0.0;
+            for (int t = 0; t < L; ++t) acc += s[t] * bf16_value(v[((size_t)g * L + t) * D + i]);
+            out[(size_t)h * D + i] = acc / den;
+        }
+        free(s);
+    }
 }

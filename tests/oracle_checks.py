@@ -343,10 +343,71 @@ def check_router_logits_identity(lib):
     assert np.array_equal(got, bf16_to_f64(x)[:, :E])
 
 
+# ---- decode attention over grouped KV heads
+
+def _attn_case(Hq, Hkv, D, L, seed):
+    return wl.make_attn_case(wl.AttnDims(Hq=Hq, Hkv=Hkv, D=D, L=L), seed=seed)
+
+
+def check_attn_torch_sdpa(lib):
+    """Against torch's scaled_dot_product_attention in float64 on the CPU, the
+    KV heads repeated over their groups of query heads (repeat_interleave:
+    query head h reads KV head h // G)."""
+    for Hq, Hkv, D, L in ((16, 2, 16, 37), (8, 1, 64, 300), (32, 4, 8, 5)):
+        c = _attn_case(Hq, Hkv, D, L, 41)
+        G = Hq // Hkv
+        q = torch.from_numpy(bf16_to_f64(c["q"])).view(1, Hq, 1, D)
+        k = torch.from_numpy(bf16_to_f64(c["k"])).repeat_interleave(G, dim=0).view(1, Hq, L, D)
+        v = torch.from_numpy(bf16_to_f64(c["v"])).repeat_interleave(G, dim=0).view(1, Hq, L, D)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v).view(Hq, D).numpy()
+        got = oracle.gqa_decode(c["q"], c["k"], c["v"], lib=lib)
+        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def check_attn_closed_forms(lib):
+    """q = 0: every score is 0, so o is the plain mean of the V rows; L = 1:
+    o is that single V row exactly; one key with a score far above the rest
+    takes all the weight (exp(-60) below fp64 resolution of the sum)."""
+    c = _attn_case(16, 2, 32, 9, 42)
+    zero = np.zeros_like(c["q"])
+    got = oracle.gqa_decode(zero, c["k"], c["v"], lib=lib)
+    means = bf16_to_f64(c["v"]).mean(axis=1)  # [Hkv][D]
+    np.testing.assert_allclose(got, np.repeat(means, 8, axis=0), rtol=1e-13, atol=1e-14)
+    c1 = _attn_case(16, 2, 32, 1, 43)
+    got1 = oracle.gqa_decode(c1["q"], c1["k"], c1["v"], lib=lib)
+    assert np.array_equal(got1, np.repeat(bf16_to_f64(c1["v"])[:, 0, :], 8, axis=0))
+    # one dominant key: k_t* = 16 q_h for every t in the group, others 0 -> s_t* = 16 |q|^2 / sqrt(D)
+    Hq, Hkv, D, L = 8, 1, 16, 6
+    q = wl.to_bf16_bits(np.full((Hq, D), 1.0, np.float32))
+    k = np.zeros((Hkv, L, D), np.uint16)
+    k[0, 4] = wl.to_bf16_bits(np.full(D, 16.0, np.float32))
+    v = _attn_case(Hq, Hkv, D, L, 44)["v"]
+    got2 = oracle.gqa_decode(q, k, v, lib=lib)
+    np.testing.assert_allclose(got2, np.repeat(bf16_to_f64(v)[:, 4, :], Hq, axis=0), rtol=0, atol=1e-12)
+
+
+def check_attn_grouping_and_order(lib):
+    """Each query head reads only its own KV head (constant V rows per KV head
+    give constant outputs per group), and reversing the cached tokens leaves
+    every output unchanged."""
+    Hq, Hkv, D, L = 24, 3, 16, 11
+    c = _attn_case(Hq, Hkv, D, L, 45)
+    v = np.empty((Hkv, L, D), np.uint16)
+    for g in range(Hkv):
+        v[g] = wl.to_bf16_bits(np.full((L, D), float(g + 1), np.float32))
+    got = oracle.gqa_decode(c["q"], c["k"], v, lib=lib)
+    np.testing.assert_allclose(got, np.repeat(np.arange(1.0, Hkv + 1.0), Hq // Hkv)[:, None] * np.ones((1, D)),
+                               rtol=1e-13)
+    a = oracle.gqa_decode(c["q"], c["k"], c["v"], lib=lib)
+    b = oracle.gqa_decode(c["q"], c["k"][:, ::-1].copy(), c["v"][:, ::-1].copy(), lib=lib)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
 ALL_CHECKS = [
     check_packing_fixture, check_rounding_fixture, check_dequant_closed_form,
     check_dequant_general_rounding, check_route_fixture, check_topk_vs_argsort,
     check_weights_special, check_counting_sort, check_block_map, check_ffn_bruteforce,
     check_ffn_single_expert_torch, check_ffn_integer, check_ffn_metamorphic, check_ffn_shared_gate,
     check_router_logits_vs_matmul, check_router_logits_identity,
+    check_attn_torch_sdpa, check_attn_closed_forms, check_attn_grouping_and_order,
 ]

@@ -34,6 +34,13 @@ MUTATIONS = [
     ("x_index", "xt[i] = bf16_value(x[(size_t)t * d + i]);", "xt[i] = bf16_value(x[(size_t)t + i]);"),
     ("router_transposed", "(double)W[(size_t)i * E + e]", "(double)W[((size_t)e * d + i) % ((size_t)d * E)]"),
     ("router_bias_dropped", "if (bias) acc += (double)bias[e];", "if (bias) acc += 0.0;"),
+    ("attn_scale_dropped", "s[t] = acc / sqrt((double)D);", "s[t] = acc;"),
+    ("attn_group_modulo", "const int g = h / G;", "const int g = h % Hkv;"),
+    ("attn_not_normalised", "out[(size_t)h * D + i] = acc / den;", "out[(size_t)h * D + i] = acc;"),
+    ("attn_v_dim_reversed", "acc += s[t] * bf16_value(v[((size_t)g * L + t) * D + i]);",
+     "acc += s[t] * bf16_value(v[((size_t)g * L + t) * D + (D - 1 - i)]);"),
+    ("attn_last_token_dropped", "for (int t = 0; t < L; ++t) {\n            s[t] = exp(s[t] - smax);",
+     "for (int t = 0; t < L; ++t) {\n            s[t] = (t == L - 1 && L > 1) ? 0.0 : exp(s[t] - smax);"),
 ]
 
 
