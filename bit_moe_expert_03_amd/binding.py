@@ -20,7 +20,8 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_SHAPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 EXPORTS = ("moe_abi_version", "moe_tile_m", "moe_max_tiles", "moe_workspace_bytes", "moe_route",
            "moe_ffn", "moe_layer", "moe_layer_kernels", "moe_layer_timed", "moe_dequant",
            "moe_router_packed_bytes", "moe_router_pack", "moe_route_x", "moe_layer_noalloc",
-           "moe_status_string", "moe_last_error")
+           "moe_status_string", "moe_last_error", "moe_gqa_workspace_bytes", "moe_gqa_decode",
+           "moe_gqa_decode_timed")
 MATS = ("gate", "up", "down", "sgate", "sup", "sdown")
 
 
@@ -32,6 +33,10 @@ class MoeError(RuntimeError):
 
 class moe_dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "E", "k", "F", "Fs", "G", "tile_m", "down_nc")]
+
+
+class moe_attn_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("Hq", "Hkv", "D", "L")]
 
 
 class moe_qmat(ctypes.Structure):
@@ -79,8 +84,13 @@ def lib():
         L.moe_dequant.argtypes = [P(moe_qmat), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
         L.moe_router_pack.argtypes = [P(moe_dims), vp, vp, vp]
         L.moe_route_x.argtypes = [P(moe_dims), vp, vp, vp, vp, P(moe_routing), vp, sz, vp]
+        L.moe_gqa_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_gqa_workspace_bytes.argtypes = [P(moe_attn_dims)]
+        L.moe_gqa_decode.argtypes = [P(moe_attn_dims), vp, vp, vp, vp, vp, sz, vp]
+        L.moe_gqa_decode_timed.argtypes = [P(moe_attn_dims), vp, vp, vp, vp, vp, sz, vp,
+                                           P(ctypes.c_void_p), ctypes.c_int32]
         for f in ("moe_route", "moe_ffn", "moe_layer", "moe_layer_timed", "moe_dequant", "moe_router_pack",
-                  "moe_route_x", "moe_layer_noalloc"):
+                  "moe_route_x", "moe_layer_noalloc", "moe_gqa_decode", "moe_gqa_decode_timed"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -240,3 +250,31 @@ def moe_dequant(q: torch.Tensor, s: torch.Tensor, b: torch.Tensor, rows: int, co
                 out: torch.Tensor, stream=None):
     m = moe_qmat(_ptr(q), _ptr(s), _ptr(b))
     _check(lib().moe_dequant(ctypes.byref(m), rows, cols, G, _ptr(out), _stream(stream)))
+
+
+def make_attn_dims(a) -> moe_attn_dims:
+    """moe_attn_dims from any object with Hq, Hkv, D, L attributes."""
+    return moe_attn_dims(a.Hq, a.Hkv, a.D, a.L)
+
+
+def moe_gqa_workspace_bytes(dims: moe_attn_dims) -> int:
+    return lib().moe_gqa_workspace_bytes(ctypes.byref(dims))
+
+
+def alloc_gqa_workspace(dims: moe_attn_dims, device="cuda") -> torch.Tensor:
+    return torch.empty(max(moe_gqa_workspace_bytes(dims), 256), dtype=torch.uint8, device=device)
+
+
+def moe_gqa_decode(dims: moe_attn_dims, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   o: torch.Tensor, ws: torch.Tensor, stream=None):
+    """o[h] = softmax(q[h] . k[h // 8] / sqrt(D)) v[h // 8]; bf16 bits in and out."""
+    _check(lib().moe_gqa_decode(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(ws),
+                                ws.numel(), _stream(stream)))
+
+
+def moe_gqa_decode_timed(dims: moe_attn_dims, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         o: torch.Tensor, ws: torch.Tensor, events, stream=None):
+    """moe_gqa_decode with events around its two kernels (at least 4 raw hipEvent_t handles)."""
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(lib().moe_gqa_decode_timed(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(ws),
+                                      ws.numel(), _stream(stream), arr, len(events)))

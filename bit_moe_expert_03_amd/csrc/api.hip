@@ -407,6 +407,62 @@ MOE_API moe_status moe_layer_timed(const moe_dims *dims, const float *logits, co
     return layer_impl(dims, logits, x, w, out, y, ws, ws_bytes, stream, &tr);
 }
 
+// ---- decode attention over grouped KV heads
+
+static bool attn_dims_ok(const moe_attn_dims *d, const char **why)
+{
+    if (!d) { *why = "dims is NULL"; return false; }
+    if (d->Hkv < 1 || d->Hkv > 128 || d->Hq != 8 * d->Hkv) { *why = "need Hq = 8 * Hkv, 1 <= Hkv <= 128"; return false; }
+    if (d->D != 64 && d->D != 128 && d->D != 256) { *why = "D not in {64, 128, 256}"; return false; }
+    if (d->L < 1 || d->L > (1 << 24)) { *why = "L outside [1, 2^24]"; return false; }
+    return true;
+}
+
+MOE_API size_t moe_gqa_workspace_bytes(const moe_attn_dims *dims)
+{
+    const char *why;
+    if (!attn_dims_ok(dims, &why)) return 0;
+    return attn_workspace_bytes(dims->Hq, dims->Hkv, dims->D, dims->L);
+}
+
+static moe_status gqa_impl(const moe_attn_dims *dims, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           uint16_t *o, void *ws, size_t ws_bytes, void *stream, EventTrace *tr)
+{
+    const char *why;
+    if (!attn_dims_ok(dims, &why)) return fail(dims ? MOE_ERR_SHAPE : MOE_ERR_ARG, "%s", why);
+    const moe_attn_dims &d = *dims;
+    const size_t qb = (size_t)d.Hq * d.D * 2, kvb = (size_t)d.Hkv * d.L * d.D * 2;
+    const size_t need = attn_workspace_bytes(d.Hq, d.Hkv, d.D, d.L);
+    if (!ptr_ok(q, qb)) return fail(MOE_ERR_ARG, "q: null or misaligned pointer");
+    if (!ptr_ok(k, kvb)) return fail(MOE_ERR_ARG, "k: null or misaligned pointer");
+    if (!ptr_ok(v, kvb)) return fail(MOE_ERR_ARG, "v: null or misaligned pointer");
+    if (!ptr_ok(o, qb)) return fail(MOE_ERR_ARG, "o: null or misaligned pointer");
+    if (!ptr_ok(ws, need)) return fail(MOE_ERR_ARG, "workspace: null or misaligned pointer");
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+    if (overlap(o, qb, q, qb) || overlap(o, qb, k, kvb) || overlap(o, qb, v, kvb) || overlap(o, qb, ws, need) ||
+        overlap(ws, need, q, qb) || overlap(ws, need, k, kvb) || overlap(ws, need, v, kvb))
+        return fail(MOE_ERR_ARG, "o or the workspace overlaps another array");
+    return hip_status(launch_gqa_decode(d.Hq, d.Hkv, d.D, d.L, q, k, v, o, ws, (hipStream_t)stream, tr),
+                      "moe_gqa_decode launch");
+}
+
+MOE_API moe_status moe_gqa_decode(const moe_attn_dims *dims, const uint16_t *q, const uint16_t *k,
+                                  const uint16_t *v, uint16_t *o, void *ws, size_t ws_bytes, void *stream)
+{
+    return gqa_impl(dims, q, k, v, o, ws, ws_bytes, stream, nullptr);
+}
+
+MOE_API moe_status moe_gqa_decode_timed(const moe_attn_dims *dims, const uint16_t *q, const uint16_t *k,
+                                        const uint16_t *v, uint16_t *o, void *ws, size_t ws_bytes,
+                                        void *stream, void *const *events, int32_t n_events)
+{
+    if (!events || n_events < 4) return fail(MOE_ERR_ARG, "events: need 4 event handles");
+    EventTrace tr;
+    tr.ev = reinterpret_cast<hipEvent_t *>(const_cast<void **>(events));
+    tr.n = n_events;
+    return gqa_impl(dims, q, k, v, o, ws, ws_bytes, stream, &tr);
+}
+
 MOE_API moe_status moe_dequant(const moe_qmat *m, int32_t rows, int32_t cols, int32_t G,
                                uint16_t *out_bf16, void *stream)
 {

@@ -89,6 +89,12 @@ hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
                          const moe_weights &w, const moe_routing &r, uint16_t *y, void *ws,
                          hipStream_t s, EventTrace *tr = nullptr);
 
+// ---- attn.hip: decode attention over grouped KV heads (8 query heads per KV head)
+int attn_chunk(int Hkv, int L);
+size_t attn_workspace_bytes(int Hq, int Hkv, int D, int L);
+hipError_t launch_gqa_decode(int Hq, int Hkv, int D, int L, const uint16_t *q, const uint16_t *k,
+                             const uint16_t *v, uint16_t *o, void *ws, hipStream_t s, EventTrace *tr = nullptr);
+
 // ---- dequant.hip
 hipError_t launch_dequant(const moe_qmat &m, int rows, int cols, int G, uint16_t *out,
                           hipStream_t s);

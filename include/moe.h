@@ -57,8 +57,9 @@ extern "C" {
 
 /* 1: route / ffn / layer; 2: optional gated shared expert (moe_weights.shared_gate);
  * 3: moe_router_pack / moe_route_x / moe_router_packed_bytes;
- * 4: moe_dims.down_nc (explicit schedule field, no environment variable). */
-#define MOE_ABI_VERSION 4
+ * 4: moe_dims.down_nc (explicit schedule field, no environment variable);
+ * 5: moe_gqa_decode / moe_gqa_decode_timed / moe_gqa_workspace_bytes. */
+#define MOE_ABI_VERSION 5
 
 #if defined(__GNUC__) || defined(__clang__)
 #define MOE_API __attribute__((visibility("default")))
@@ -266,6 +267,39 @@ MOE_API const char *moe_status_string(moe_status s);
 
 /* Detail of the last non-OK status returned on this host thread. */
 MOE_API const char *moe_last_error(void);
+
+/* ---- Decode attention over grouped KV heads (a second decode workload) -----
+ * One decode token attends over L cached tokens, and eight query heads share
+ * one KV head (page "Perplexity's Lily Beats MLX-LM by 1.35x Running Qwen3.6
+ * on Apple Silicon", section "Decode optimizations"); every cached K and V
+ * row is read from memory once for its eight heads.  The pages do not write
+ * the formula; this is scaled dot-product attention:
+ *   o[h] = sum_t softmax_t(q[h] . k[g][t] / sqrt(D)) v[g][t],  g = h / 8,
+ * fp32 arithmetic from bf16 inputs, o rounded to bf16 (nearest even).
+ * Supported: Hkv >= 1, Hq = 8 * Hkv, Hq <= 1024; D in {64, 128, 256};
+ * 1 <= L <= 2^24. */
+typedef struct {
+    int32_t Hq, Hkv, D, L;
+} moe_attn_dims;
+
+/* Host-only, pure.  Workspace bytes of moe_gqa_decode (fp32 partial results
+ * of the context splits); 0 for invalid dims. */
+MOE_API size_t moe_gqa_workspace_bytes(const moe_attn_dims *dims);
+
+/* q bf16 [Hq][D]; k, v bf16 [Hkv][L][D] (one row per cached token); o bf16
+ * [Hq][D], caller-owned; ws: moe_gqa_workspace_bytes() bytes, any contents
+ * (fully rewritten by each call).  Two kernels on `stream` (context splits,
+ * then their combination); results are deterministic.  o must not overlap
+ * the inputs or ws.  Invalid arguments return a status with nothing enqueued. */
+MOE_API moe_status moe_gqa_decode(const moe_attn_dims *dims, const uint16_t *q, const uint16_t *k,
+                                  const uint16_t *v, uint16_t *o, void *ws, size_t ws_bytes, void *stream);
+
+/* Measurement form of moe_gqa_decode: kernel i (0: splits, 1: combine) is
+ * launched with events[2i] and events[2i+1] as its start and stop events;
+ * needs n_events >= 4.  Not for use under stream capture. */
+MOE_API moe_status moe_gqa_decode_timed(const moe_attn_dims *dims, const uint16_t *q, const uint16_t *k,
+                                        const uint16_t *v, uint16_t *o, void *ws, size_t ws_bytes,
+                                        void *stream, void *const *events, int32_t n_events);
 
 #ifdef __cplusplus
 }

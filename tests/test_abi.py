@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = B.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert B.moe_abi_version() == 4
+    assert B.moe_abi_version() == 5
 
 
 def test_status_strings():
@@ -177,3 +177,39 @@ def test_noalloc_limit_matches_the_header():
     text = open(HEADER).read()
     m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+
+
+def test_gqa_workspace_and_argument_checks():
+    """Decode attention: workspace holds fp32 (o, max, sum) per split and
+    query head; unsupported dims give 0 bytes and MOE_ERR_SHAPE, null,
+    misaligned or overlapping pointers and a small workspace are refused
+    before anything is launched."""
+    L = B.lib()
+    a = B.make_attn_dims(wl.ATTN_CONFIGS["attn_L32768"])
+    need = B.moe_gqa_workspace_bytes(a)
+    # 4 KV heads x 32768 tokens over ~1024 blocks: 128 tokens per split, 256 splits
+    assert need == 256 * 32 * (128 + 2) * 4
+    assert B.moe_gqa_workspace_bytes(B.moe_attn_dims(32, 4, 128, 1)) == 1 * 32 * 130 * 4
+    for bad in [(33, 4, 128, 64), (32, 4, 96, 64), (32, 4, 128, 0), (0, 0, 128, 64), (8 * 129, 129, 64, 8),
+                (32, 4, 128, (1 << 24) + 1)]:
+        d = B.moe_attn_dims(*bad)
+        assert B.moe_gqa_workspace_bytes(d) == 0, bad
+        st = L.moe_gqa_decode(ctypes.byref(d), _fake_ptr(1), _fake_ptr(2), _fake_ptr(3), _fake_ptr(4),
+                              _fake_ptr(5), 1 << 30, None)
+        assert st == B.MOE_ERR_SHAPE, bad
+    assert L.moe_gqa_decode(None, None, None, None, None, None, 0, None) == B.MOE_ERR_ARG
+    args = [_fake_ptr(i) for i in range(1, 6)]
+    for i in range(5):
+        for broken in (None, args[i] + 4):
+            t = list(args)
+            t[i] = broken
+            assert L.moe_gqa_decode(ctypes.byref(a), *t, need, None) == B.MOE_ERR_ARG, (i, broken)
+    assert L.moe_gqa_decode(ctypes.byref(a), *args, need - 1, None) == B.MOE_ERR_WORKSPACE
+    # o inside k
+    kv = 4 * 32768 * 128 * 2
+    t = list(args)
+    t[3] = args[1] + kv - 256
+    assert L.moe_gqa_decode(ctypes.byref(a), *t, need, None) == B.MOE_ERR_ARG
+    assert b"overlap" in L.moe_last_error()
+    ev = (ctypes.c_void_p * 3)()
+    assert L.moe_gqa_decode_timed(ctypes.byref(a), *args, need, None, ev, 3) == B.MOE_ERR_ARG

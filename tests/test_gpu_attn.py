@@ -1,0 +1,163 @@
+"""GPU parity of decode attention over grouped KV heads (moe_gqa_decode,
+through the C ABI) against the CPU oracle's fp64 attention.
+
+Tolerance, per element: |o - o_ref| <= 2^-8 |o_ref| + 1e-5 max|v|.  The
+kernel's result is fp32 rounded once to bf16 (nearest even): that rounding
+alone moves o by up to 2^-9 |o|, and the first term holds it with a factor of
+two to spare.  The fp32 arithmetic before it (bf16 products exact in fp32,
+sums of a few hundred terms along any path: the token slots of a lane, the
+lane and wave trees, then the splits in order) has errors of a few 2^-24 of
+the largest |v| in a random walk, about 1e-6 max|v| at these sizes; the
+second term allows ten times that, and still fails a dropped or doubled token
+at every small L here (one token moves o by about max|v| / L).  Cases where
+the result is exact (L = 1, equal scores over integer-valued V) are compared
+bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_moe_expert_03_amd import binding as B
+from bit_moe_expert_03_amd import workload as wl
+from gpu_util import Guarded, bf16_to_f64, dev, host_u16
+
+pytestmark = pytest.mark.gpu
+
+A = wl.AttnDims
+# ragged lengths (one token, fewer tokens than a block takes, a last block of
+# 1 or of a few tokens), every head dimension, one KV head and the most KV
+# heads the entry point takes, and block sizes from 64 to 1024 tokens
+SMALL = {
+    "L1_D128": A(Hq=8, Hkv=1, D=128, L=1),
+    "L5_D64_Hkv2": A(Hq=16, Hkv=2, D=64, L=5),
+    "L63_D256": A(Hq=8, Hkv=1, D=256, L=63),
+    "L65_tail1": A(Hq=32, Hkv=4, D=128, L=65),
+    "L1000_D64_Hkv3": A(Hq=24, Hkv=3, D=64, L=1000),
+    "L3000_D256_Hkv2": A(Hq=16, Hkv=2, D=256, L=3000),
+    "Hkv128_L200_D64": A(Hq=1024, Hkv=128, D=64, L=200),
+    "L70001_chunk128": A(Hq=8, Hkv=1, D=128, L=70001),
+    "L600001_chunk1024_D64": A(Hq=8, Hkv=1, D=64, L=600001),
+    "L300001_chunk512_D256": A(Hq=8, Hkv=1, D=256, L=300001),
+}
+
+
+def _case(name):
+    if name in wl.ATTN_CONFIGS:
+        return wl.make_attn_case(name)
+    return wl.make_attn_case(SMALL[name], seed=300 + list(SMALL).index(name))
+
+
+def run_attn(c, ws_fill=0xFF):
+    """moe_gqa_decode on the case's inputs; output and workspace sit in guard
+    bands, the output pre-filled with a NaN pattern and the workspace with
+    garbage (its contents on entry do not matter)."""
+    d = c["dims"]
+    ad = B.make_attn_dims(d)
+    q, k, v = dev(c["q"]), dev(c["k"]), dev(c["v"])
+    go = Guarded((d.Hq, d.D), torch.int16, fill=0x7FC1)
+    gws = Guarded((B.moe_gqa_workspace_bytes(ad),), torch.uint8, fill=ws_fill)
+    B.moe_gqa_decode(ad, q, k, v, go.t, gws.t)
+    torch.cuda.synchronize()
+    go.check("o")
+    gws.check("workspace")
+    return host_u16(go.t)
+
+
+def check_o(c, o_bits):
+    ref = oracle.gqa_decode(c["q"], c["k"], c["v"])
+    o = bf16_to_f64(o_bits)
+    assert np.all(np.isfinite(o)), "non-finite output"
+    vmax = np.abs(bf16_to_f64(c["v"])).max()
+    err = np.abs(o - ref)
+    tol = 2.0 ** -8 * np.abs(ref) + 1e-5 * vmax
+    worst = np.unravel_index(np.argmax(err / tol), err.shape)
+    assert np.all(err <= tol), (f"head {worst[0]} dim {worst[1]}: o {o[worst]} ref {ref[worst]} "
+                                f"err {err[worst]:.3e} tol {tol[worst]:.3e}")
+    return float((err / tol).max())
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_attn_small_shapes(name):
+    c = _case(name)
+    check_o(c, run_attn(c))
+
+
+@pytest.mark.parametrize("name", list(wl.ATTN_CONFIGS))
+def test_attn_workloads_all_heads(name):
+    c = _case(name)
+    check_o(c, run_attn(c))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_attn_single_token_returns_its_value_row(D):
+    """L = 1: the one weight is exactly 1, so o[h] is v[h // 8][0] bit for bit."""
+    c = wl.make_attn_case(A(Hq=16, Hkv=2, D=D, L=1), seed=11)
+    o = run_attn(c)
+    np.testing.assert_array_equal(o, np.repeat(c["v"][:, 0, :], 8, axis=0))
+
+
+def test_attn_equal_scores_at_the_largest_length():
+    """L = 2^24 (the largest the entry point takes), K = 0: every score is 0,
+    every weight exactly 1, and o is the mean of the V rows.  With
+    v[t][d] = ((t + d) mod 7) - 3 every partial sum is a small integer, so the
+    kernel's fp32 sums are exact; whole periods of 7 cancel and L = 7 m + 1
+    leaves the first row, o[h][d] = ((d mod 7) - 3) / 2^24, which bf16 holds
+    exactly."""
+    L, D, Hkv = 1 << 24, 64, 1
+    ad = B.moe_attn_dims(8 * Hkv, Hkv, D, L)
+    rng = np.random.default_rng(5)
+    q = dev(wl.to_bf16_bits(rng.standard_normal((8, D), dtype=np.float32)))
+    k = torch.zeros((Hkv, L, D), dtype=torch.bfloat16, device="cuda").view(torch.int16)
+    t = torch.arange(L, dtype=torch.int32, device="cuda")[:, None]
+    dd = torch.arange(D, dtype=torch.int32, device="cuda")[None, :]
+    v = (((t + dd) % 7) - 3).to(torch.bfloat16).view(torch.int16).reshape(Hkv, L, D).contiguous()
+    del t
+    o = torch.full((8, D), 0x7FC1, dtype=torch.int16, device="cuda")
+    ws = B.alloc_gqa_workspace(ad)
+    B.moe_gqa_decode(ad, q, k, v, o, ws)
+    torch.cuda.synchronize()
+    want = ((np.arange(D) % 7) - 3) / float(L)
+    np.testing.assert_array_equal(bf16_to_f64(host_u16(o)), np.broadcast_to(want, (8, D)))
+
+
+def test_attn_deterministic_timed_and_graph_replay():
+    """Two calls give the same bits whatever the workspace held; the timed
+    entry point gives the same bits and two positive kernel times; a captured
+    graph replays to the same bits, with eager calls between replays."""
+    c = _case("attn_L32768")
+    d = c["dims"]
+    ad = B.make_attn_dims(d)
+    a = run_attn(c, ws_fill=0xFF)
+    b = run_attn(c, ws_fill=0x00)
+    np.testing.assert_array_equal(a, b)
+    q, k, v = dev(c["q"]), dev(c["k"]), dev(c["v"])
+    o = torch.empty((d.Hq, d.D), dtype=torch.int16, device="cuda")
+    ws = B.alloc_gqa_workspace(ad)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    B.moe_gqa_decode_timed(ad, q, k, v, o, ws, [e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u16(o), a)
+    times = [evs[0].elapsed_time(evs[1]), evs[2].elapsed_time(evs[3])]
+    assert all(t > 0 for t in times), times
+    with pytest.raises(B.MoeError):
+        B.moe_gqa_decode_timed(ad, q, k, v, o, ws, [e.cuda_event for e in evs[:3]])
+
+    s = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr, stream=s):
+            B.moe_gqa_decode(ad, q, k, v, o, ws, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.fill_(0x7FC1)
+        ws.fill_(0xFF)
+        gr.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_u16(o), a, err_msg=f"replay {rep}")
+        B.moe_gqa_decode(ad, q, k, v, torch.empty_like(o), B.alloc_gqa_workspace(ad))
+        torch.cuda.synchronize()
