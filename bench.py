@@ -13,7 +13,9 @@ K timed steps are one HIP graph of K layer calls.
 
 Further objects: `prefill` (T = 4096 tokens with Zipf-skewed routing, the
 prefill half of the metric), `prefill512` (T = 512) and `prefill32768`
-(T = 32768), one weight set each, timed the same way.  The decode graph
+(T = 32768), one weight set each, timed the same way; `attention`: the
+second decode workload, attention of one token over grouped KV heads at
+three cache lengths (context, not the metric).  The decode graph
 visits min(K, 40) weight sets and the caches are flushed before every timed
 replay, so the weights always come from HBM.
 
@@ -388,6 +390,95 @@ def bench_route_x(B, wl, c, dm, reps=20):
     return res
 
 
+def attn_bytes(a):
+    """Algorithmic bytes of one decode-attention call: the K and V caches of
+    every KV head, q read and o written (bf16); the kernels' fp32 partials
+    are the implementation's, not the algorithm's."""
+    return 2 * a.Hkv * a.L * a.D * 2 + 2 * a.Hq * a.D * 2
+
+
+def bench_attn(B, wl, args, name, calls=200):
+    """Context, the second decode workload: attention of one token over a
+    KV cache of L tokens, eight query heads per KV head.  Distinct KV caches
+    (the layers of a model) rotate per call, about 2 GiB in all, so every
+    call streams its cache from HBM.  Timed: one HIP graph of `calls` calls
+    (median of three replays); per-kernel times from event pairs on the
+    same calls run eagerly behind a spin kernel."""
+    import torch
+    a = wl.ATTN_CONFIGS[name]
+    ad = B.make_attn_dims(a)
+    per = attn_bytes(a)
+    nsets = max(2, min(calls, -(-(2 << 30) // per)))
+    c = wl.make_attn_case(name)
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    sets = [(to_dev(c["k"]), to_dev(c["v"]))]
+    for _ in range(nsets - 1):
+        kv = torch.randn((2, a.Hkv, a.L, a.D), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+        sets.append((kv[0], kv[1]))
+    q = to_dev(c["q"])
+    o = torch.empty((a.Hq, a.D), dtype=torch.int16, device="cuda")
+    ws = B.alloc_gqa_workspace(ad)
+    for i in range(3):
+        B.moe_gqa_decode(ad, q, sets[i % nsets][0], sets[i % nsets][1], o, ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(calls):
+                B.moe_gqa_decode(ad, q, sets[i % nsets][0], sets[i % nsets][1], o, ws, stream=stream)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        reps.append(time.perf_counter() - t0)
+    sec = sorted(reps)[1] / calls
+    evs = [make_events(4) for _ in range(calls)]
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(200_000_000)
+        for i in range(calls):
+            B.moe_gqa_decode_timed(ad, q, sets[i % nsets][0], sets[i % nsets][1], o, ws,
+                                   [e.cuda_event for e in evs[i]], stream=stream)
+    torch.cuda.synchronize()
+    per_kernel = [sum(ev[2 * j].elapsed_time(ev[2 * j + 1]) for ev in evs) / calls for j in range(2)]
+    achieved = per / (per_kernel[0] * 1e-3) / 1e9
+    out = {
+        "workload": f"decode attention, one token over L={a.L} cached tokens, Hq={a.Hq} query heads on "
+                    f"Hkv={a.Hkv} KV heads (8 per KV head), D={a.D}, bf16 K/V cache, {nsets} caches rotated",
+        "us_per_call": sec * 1e6,
+        "calls_per_s": 1.0 / sec,
+        "gbs_per_call": per / sec / 1e9,
+        "bytes_per_call": per,
+        "per_kernel_us": {"gqa_partial": per_kernel[0] * 1e3, "gqa_combine": per_kernel[1] * 1e3},
+        "roofline": {"bound": "hbm", "kernel": "gqa_partial_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("gqa_partial_kernel_" + name.split("_")[-1]),
+                     "bytes_per_launch": per, "avg_launch_ms": per_kernel[0]},
+    }
+    log(f"attention {name}: {sec * 1e6:.2f} us/call ({out['gbs_per_call']:.0f} GB/s), partial "
+        f"{per_kernel[0] * 1e3:.2f} us ({achieved:.0f} GB/s), combine {per_kernel[1] * 1e3:.2f} us")
+    if not args.no_cpu_baseline:
+        import oracle
+        t0, n = time.perf_counter(), 0
+        while True:
+            oracle.gqa_decode(c["q"], c["k"], c["v"])
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds / 4:
+                break
+        out["cpu_baseline"] = {"value": n / el, "unit": "calls/s", "cores": oracle.threads(), "kind": "oracle",
+                               "sample": f"{n} fp64 oracle calls on the first cache of this workload "
+                                         "(OpenMP over query heads)"}
+    del sets, g
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline_decode(wl, host, seconds):
     """The oracle on decode tokens: each call routes and runs the fp64 FFN of
     a batch of independent T = 1 decode steps that share one weight set, so
@@ -442,6 +533,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-small-batches", action="store_true",
                     help="skip the few-token batch context (counter passes keep the decode kernels at T=1)")
+    ap.add_argument("--no-attn", action="store_true", help="skip the decode-attention context")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="first run a plain copy kernel of this many MB (scale for counter passes)")
@@ -474,6 +566,9 @@ def main():
                 out["cpu_baseline"] = cpu_baseline_prefill(wl, case, args.cpu_seconds)
             pre[key] = out
             del case
+    attn = None
+    if not args.no_attn:
+        attn = {name: bench_attn(B, wl, args, name) for name in wl.ATTN_CONFIGS}
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -501,6 +596,7 @@ def main():
         "prefill": pre.get("prefill"),
         "prefill512": pre.get("prefill512"),
         "prefill32768": pre.get("prefill32768"),
+        "attention": attn,
         "achievable": peaks,
     }
     print(json.dumps(line), flush=True)

@@ -1,44 +1,58 @@
 // Decode attention of one token over grouped KV heads (gfx950): the second
 // decode workload of the pages.  Eight query heads share one KV head, and
-// the pages pack query heads that share a KV head into one threadgroup so
-// that they share the KV loads (page "Perplexity's Lily Beats MLX-LM by 1.35x
-// Running Qwen3.6 on Apple Silicon", section "Decode optimizations").  Here
-// all eight query heads of a KV head live in every wave: each K and V row is
-// read from HBM once and used by the eight heads in registers.
+// the pages pack four of them into one threadgroup so that they share the
+// KV loads (page "Perplexity's Lily Beats MLX-LM by 1.35x Running Qwen3.6 on
+// Apple Silicon", section "Decode optimizations").  Here all eight query
+// heads of a KV head are the columns of one matrix-core tile: each K and V
+// row is read from HBM once and used by all eight heads.
 //
-// o_h = sum_t softmax_t(q_h . k_{g,t} / sqrt(D)) v_{g,t}, g = h / 8, fp32
-// arithmetic from bf16 inputs, bf16 output.  One token reads 2 L D bytes per
-// KV head and does 8 D multiply-adds per cached token for the scores and as
-// many for the output: about 4 per byte, so the step is bound by HBM, and
-// the products run on the vector ALUs (v_dot2_f32_bf16 for the scores, fp32
-// fma for the output) rather than being reshaped into matrix-core tiles.
+// o_h = sum_t softmax_t(q_h . k_{g,t} / sqrt(D)) v_{g,t}, g = h / 8, bf16
+// inputs, fp32 accumulation, bf16 output.  One token reads 2 L D bytes per
+// KV head, so the step is bound by HBM.  On the vector ALUs the products
+// would cost about as many cycles as the bytes take to arrive (8 heads x 2
+// products per bf16 element), so the two contractions run on the matrix
+// cores, with the eight heads padded to a 16-wide tile:
+//   scores  S^T = K Q^T     v_mfma_f32_16x16x32_bf16: rows = 16 tokens,
+//                           columns = heads, K = head dims (bf16 products
+//                           are exact in fp32);
+//   output  O^T = V^T P^T   rows = 16 head dims, columns = heads, K = 32
+//                           tokens.  P is split into bf16 hi + lo parts
+//                           (two MFMAs), which keeps about 16 bits of each
+//                           weight, so the output carries fp32-level error.
+// The score tile leaves lane l with head l % 16 and tokens 4 (l / 16) + i,
+// which is exactly a B operand of the output MFMA once the 32 tokens of two
+// score tiles are ordered tau(g, k) = 16 (k / 4) + 4 g + k % 4: the weights
+// never leave the lane.  V^T is formed in registers: lane (r, g) loads dims
+// D/16 r .. of its eight tokens tau(g, .) and interleaves them pairwise (one
+// bit-select per output word), so every A operand is one token-contiguous
+// column of V; row r of output tile n is head dim (D/16) r + n.
 //
 // Kernels (stream-ordered):
-//   gqa_partial_kernel<D>   grid (splits, Hkv), 4 waves: the block's C cached
-//                           tokens (C a power of two, chosen so that the grid
-//                           holds about 1024 blocks).  Lane l of a wave owns 8
-//                           dims (8 (l % (D/8)) ..) of token l / (D/8) of an
-//                           iteration of 64 / (D/8) tokens.  Pass 1: scores of
-//                           the 8 heads (dot2 over the lane's dims, then a
-//                           transpose-reduce over the token's lanes: 8 values
-//                           halve at each exchange, so 8 exchanges instead of
-//                           32 leave each lane one head's full score) into
-//                           LDS; block max and exp2 weights per head.  Pass 2:
-//                           o_h += p_t v_t for the lane's dims, summed over the
-//                           token slots and waves at the end.  Writes the
-//                           block's (max, sum, unnormalised o) per head.
-//   gqa_combine_kernel      one block per query head, one thread per dim: the
-//                           splits' partials rescaled to the global max and
-//                           summed in split order (deterministic), o = sum /
-//                           weight sum, rounded to bf16.
+//   gqa_partial_kernel<D>   grid (splits, Hkv), 4 waves, one round of blocks
+//                           (blocks per CU from the occupancy of the kernel
+//                           times the CUs); a block takes C consecutive
+//                           tokens (C a multiple of 128), its waves take
+//                           interleaved 32-token slices, each with its own
+//                           online softmax (running max per head, rescale of
+//                           the accumulators when it grows), so the main
+//                           loop has no block barrier.  The four waves are
+//                           merged through LDS; writes the block's (max,
+//                           weight sum, unnormalised o) per query head.
+//   gqa_combine_kernel      grid (Hq, D/16): the splits' partials rescaled to
+//                           the global max and summed in a fixed order
+//                           (deterministic), o = sum / weight sum, bf16.
 #include "moe_device.h"
 #include "moe_internal.h"
 
+#include <atomic>
+
 namespace moe {
 
-constexpr int kAttnG = 8;          // query heads per KV head
-constexpr int kAttnThreads = 256;  // 4 waves
-constexpr int kAttnUnroll = 8;     // iterations whose rows are loaded together
+constexpr int kAttnG = 8;            // query heads per KV head
+constexpr int kAttnThreads = 256;    // 4 waves
+constexpr int kAttnSlice = 32;       // tokens per wave iteration
+constexpr int kAttnMaxSplits = 1024;
+constexpr int kAttnCombineThreads = 256;
 
 struct AttnArgs {
     const uint16_t *q, *k, *v;  // [Hq][D], [Hkv][L][D], [Hkv][L][D]
@@ -48,235 +62,300 @@ struct AttnArgs {
     float *part_ml;             // [nsplit][Hq][2]: block max (log2 domain), weight sum
 };
 
-// Transpose-reduce of 8 per-lane partial sums over the LPT lanes of a token
-// (lanes l .. l + LPT - 1 of an aligned group): at exchange distance w the
-// lane keeps half of its values (the half chosen by its lane bit w) and adds
-// the partner's copies of them, so the count halves at each step; after
-// log2(LPT) steps every lane holds the full sum of one head, head index
-// given by its low lane bits (LPT >= 8).
-template <int LPT>
-__device__ __forceinline__ float reduce8_over_token(float (&a)[8], int &head)
+// K and V rows are read once per call: non-temporal loads (nt bit), so the
+// stream does not displace the caches' other contents
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_stream4(const uint16_t *p)
 {
-    const int lane = threadIdx.x & 63;
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = a[i];
-    int n = 8;       // live values
-    int base = 0;    // head index of v[0]
-#pragma unroll
-    for (int w = LPT / 2; w >= 1; w >>= 1) {
-        if (n > 1) {
-            const bool upper = (lane & w) != 0;
-            const int h = n / 2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i < h) {
-                    // send the half the partner keeps, receive the half this lane keeps
-                    const float send = upper ? v[i] : v[i + h];
-                    const float keep = upper ? v[i + h] : v[i];
-                    v[i] = keep + __shfl_xor(send, w);
-                }
-            }
-            base += upper ? h : 0;
-            n = h;
-        } else {
-            v[0] += __shfl_xor(v[0], w);
-        }
-    }
-    head = base;
-    return v[0];
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 load_stream2(const uint16_t *p)
+{
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(v[0], v[1]);
+}
+
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void gqa_partial_kernel(AttnArgs a)
+__global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a)
 {
-    constexpr int LPT = D / 8;      // lanes per token
-    constexpr int TPI = 64 / LPT;   // tokens per wave iteration
-    __shared__ float s_p[kAttnThreads / 64 * 1024 / 4 * kAttnG];  // scores, then weights: [token][head]
-    __shared__ float s_m[kAttnG], s_l[kAttnG], s_red[4][kAttnG];
+    constexpr int DPL = D / 16;  // head dims per lane in the output tiles (= number of tiles)
+    constexpr int VW = DPL / 2;  // words of V per lane and token
+    constexpr int KK = D / 32;   // score MFMAs per 16-token tile
     __shared__ float s_o[4][kAttnG][D];
+    __shared__ float s_m[4][kAttnG], s_l[4][kAttnG];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, grp = lane >> 4;
     const int split = blockIdx.x, g = blockIdx.y;
     const int t0 = split * a.C, n = min(a.C, a.L - t0);  // tokens of the block (>= 1)
-    const int per_wave = a.C / 4;                          // tokens per wave (a multiple of TPI)
-    const int slot = lane / LPT, dpart = lane % LPT;       // token slot, 8-dim part
-    const size_t kvbase = ((size_t)g * a.L) * D + 8 * dpart;
+    const uint16_t *kb = a.k + ((size_t)g * a.L + t0) * D;
+    const uint16_t *vb = a.v + ((size_t)g * a.L + t0) * D;
+    const bool head_ok = r < kAttnG;  // columns 8..15 of the tiles are padding
 
-    // q of the 8 heads, this lane's 8 dims: 4 bf16 pairs per head
-    uint32_t qr[kAttnG][4];
+    // B operand of the scores: column r = query head 8 g + r, K chunk kk =
+    // dims 32 kk + 8 grp .. + 7 (the A operand takes the same dims)
+    uint4 qb[KK];
 #pragma unroll
-    for (int h = 0; h < kAttnG; ++h) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(a.q + (size_t)(kAttnG * g + h) * D + 8 * dpart);
-        qr[h][0] = u.x; qr[h][1] = u.y; qr[h][2] = u.z; qr[h][3] = u.w;
-    }
+    for (int kk = 0; kk < KK; ++kk)
+        qb[kk] = head_ok ? *reinterpret_cast<const uint4 *>(a.q + (size_t)(kAttnG * g + r) * D + 32 * kk + 8 * grp)
+                         : make_uint4(0, 0, 0, 0);
 
-    // pass 1: scores (log2 domain) of the wave's tokens into LDS
-    for (int it0 = 0; it0 < per_wave; it0 += TPI * kAttnUnroll) {
-        uint4 kr[kAttnUnroll];
+    f32x4 oacc[DPL];
 #pragma unroll
-        for (int u = 0; u < kAttnUnroll; ++u) {
-            const int tl = wave * per_wave + it0 + TPI * u + slot;  // token inside the block
-            const int tt = t0 + min(tl, n - 1);                      // past the end: a valid row
-            kr[u] = *reinterpret_cast<const uint4 *>(a.k + kvbase + (size_t)tt * D);
+    for (int i = 0; i < DPL; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int base = kAttnSlice * wave; base < n; base += 4 * kAttnSlice) {
+        // K rows of the two 16-token tiles (row r of tile j = token base + 16 j + r);
+        // past the block's last token, the last valid row is read and its score masked
+        uint4 kr[2][KK];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int t = min(base + 16 * j + r, n - 1);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                kr[j][kk] = load_stream4(kb + (size_t)t * D + 32 * kk + 8 * grp);
         }
+        // V of tokens tau(grp, k), dims DPL r .. DPL r + DPL - 1
+        uint32_t vw[8][VW];
 #pragma unroll
-        for (int u = 0; u < kAttnUnroll; ++u) {
-            const int tl = wave * per_wave + it0 + TPI * u + slot;
-            float part[kAttnG];
+        for (int k = 0; k < 8; ++k) {
+            const int t = min(base + 16 * (k >> 2) + 4 * grp + (k & 3), n - 1);
+            const uint16_t *src = vb + (size_t)t * D + DPL * r;
+            if constexpr (VW == 2) {
+                const uint2 u = load_stream2(src);
+                vw[k][0] = u.x; vw[k][1] = u.y;
+            } else {
 #pragma unroll
-            for (int h = 0; h < kAttnG; ++h) {
-                float acc = dot2_bf16(kr[u].x, qr[h][0], 0.f);
-                acc = dot2_bf16(kr[u].y, qr[h][1], acc);
-                acc = dot2_bf16(kr[u].z, qr[h][2], acc);
-                part[h] = dot2_bf16(kr[u].w, qr[h][3], acc);
+                for (int c = 0; c < VW / 4; ++c) {
+                    const uint4 u = load_stream4(src + 8 * c);
+                    vw[k][4 * c] = u.x; vw[k][4 * c + 1] = u.y; vw[k][4 * c + 2] = u.z; vw[k][4 * c + 3] = u.w;
+                }
             }
-            int head;
-            const float s = reduce8_over_token<LPT>(part, head) * a.scale2;
-            // the lanes whose bits below the three halving exchanges are 0 hold
-            // the 8 heads once each
-            if ((dpart & (LPT / 8 - 1)) == 0 && it0 + TPI * u < per_wave)
-                s_p[tl * kAttnG + head] = tl < n ? s : -INFINITY;
         }
-    }
-    __syncthreads();
 
-    // block max and weight sum per head: thread (part = tid / 8, head h =
-    // tid % 8) takes tokens part, part + 32, ...; the 32 parts of a head are
-    // combined over the lanes of a wave (exchanges 8, 16, 32) and then over
-    // the 4 waves in order, so the sums are deterministic.  The scores
-    // become the weights exp2(s - max), 0 past the block's last token.
-    {
-        const int h = tid & (kAttnG - 1), part = tid >> 3;
-        float m = -INFINITY;
-        for (int t = part; t < n; t += 32) m = fmaxf(m, s_p[t * kAttnG + h]);
-        m = fmaxf(m, __shfl_xor(m, 8));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        if (lane < kAttnG) s_red[wave][lane] = m;
-        __syncthreads();
-        m = fmaxf(fmaxf(s_red[0][h], s_red[1][h]), fmaxf(s_red[2][h], s_red[3][h]));
-        float l = 0.f;
-        for (int t = part; t < a.C; t += 32) {
-            const float p = t < n ? exp2f(s_p[t * kAttnG + h] - m) : 0.f;
-            s_p[t * kAttnG + h] = p;
-            l += p;
+        // scores: lane holds head r, tokens base + 16 j + 4 grp + i
+        f32x4 sc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) sc[j] = mfma16(kr[j][kk], qb[kk], sc[j]);
         }
-        l += __shfl_xor(l, 8);
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        __syncthreads();  // every wave has read s_red (the maxima)
-        if (lane < kAttnG) s_red[wave][lane] = l;
-        __syncthreads();
-        if (tid < kAttnG) {
-            s_m[tid] = m;
-            s_l[tid] = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+        float s[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int t = base + 16 * (k >> 2) + 4 * grp + (k & 3);
+            s[k] = (head_ok && t < n) ? sc[k >> 2][k & 3] * a.scale2 : -INFINITY;
+            mx = fmaxf(mx, s[k]);
         }
-    }
-    __syncthreads();
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == m_run ? 1.f : exp2f(m_run - m_new);  // 1 while nothing is valid
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) oacc[i] *= alpha;
+            l_run *= alpha;
+        }
+        m_run = m_new;
 
-    // pass 2: o_h += p_t v_t over the wave's tokens, this lane's 8 dims
-    float o[kAttnG][8];
+        // weights and their bf16 hi / lo parts: B operand of the output MFMAs
+        // (K position k = token tau(grp, k))
+        uint32_t ph[4], pl[4];
 #pragma unroll
-    for (int h = 0; h < kAttnG; ++h)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[h][j] = 0.f;
-    for (int it0 = 0; it0 < per_wave; it0 += TPI * kAttnUnroll) {
-        uint4 vr[kAttnUnroll];
-#pragma unroll
-        for (int u = 0; u < kAttnUnroll; ++u) {
-            const int tl = wave * per_wave + it0 + TPI * u + slot;
-            const int tt = t0 + min(tl, n - 1);
-            vr[u] = *reinterpret_cast<const uint4 *>(a.v + kvbase + (size_t)tt * D);
+        for (int w = 0; w < 4; ++w) {
+            const float p0 = s[2 * w] == -INFINITY ? 0.f : exp2f(s[2 * w] - m_new);
+            const float p1 = s[2 * w + 1] == -INFINITY ? 0.f : exp2f(s[2 * w + 1] - m_new);
+            l_run += p0 + p1;
+            ph[w] = pack_bf16x2(p0, p1);
+            pl[w] = pack_bf16x2(p0 - __uint_as_float(ph[w] << 16), p1 - __uint_as_float(ph[w] & 0xFFFF0000u));
         }
+        const uint4 bh = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+        const uint4 bl = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+
+        // output tiles: A operand of tile nt = dim DPL r + nt of tokens tau(grp, 0..7)
 #pragma unroll
-        for (int u = 0; u < kAttnUnroll; ++u) {
-            if (it0 + TPI * u >= per_wave) break;
-            const int tl = wave * per_wave + it0 + TPI * u + slot;
-            const float4 p0 = *reinterpret_cast<const float4 *>(&s_p[tl * kAttnG]);
-            const float4 p1 = *reinterpret_cast<const float4 *>(&s_p[tl * kAttnG + 4]);
-            const float p[kAttnG] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};  // 0 past the end
-            const uint32_t w4[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
-            float vf[8];
+        for (int nt = 0; nt < DPL; ++nt) {
+            uint32_t av[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                vf[2 * j] = bf16_to_f32(w4[j] & 0xFFFFu);
-                vf[2 * j + 1] = bf16_to_f32(w4[j] >> 16);
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x = vw[2 * w][nt >> 1], y = vw[2 * w + 1][nt >> 1];
+                av[w] = (nt & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
             }
-#pragma unroll
-            for (int h = 0; h < kAttnG; ++h)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) o[h][j] = __builtin_fmaf(p[h], vf[j], o[h][j]);
+            const uint4 au = make_uint4(av[0], av[1], av[2], av[3]);
+            oacc[nt] = mfma16(au, bh, oacc[nt]);
+            oacc[nt] = mfma16(au, bl, oacc[nt]);
         }
     }
-    // sum over the wave's token slots (lanes with equal dpart), then over waves
+
+    // merge the waves: lane (r, grp) holds o[head r][DPL (4 grp + i) + nt]
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (head_ok) {
 #pragma unroll
-    for (int w = LPT; w < 64; w <<= 1)
+        for (int nt = 0; nt < DPL; ++nt)
 #pragma unroll
-        for (int h = 0; h < kAttnG; ++h)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[h][j] += __shfl_xor(o[h][j], w);
-    if (slot == 0) {
-#pragma unroll
-        for (int h = 0; h < kAttnG; ++h)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) s_o[wave][h][8 * dpart + j] = o[h][j];
+            for (int i = 0; i < 4; ++i) s_o[wave][r][DPL * (4 * grp + i) + nt] = oacc[nt][i];
+        if (grp == 0) {
+            s_m[wave][r] = m_run;
+            s_l[wave][r] = l_run;
+        }
     }
     __syncthreads();
-    const int hq0 = kAttnG * g;
+    const int hq0 = kAttnG * g, Hq = kAttnG * a.Hkv;
     for (int i = tid; i < kAttnG * D; i += kAttnThreads) {
         const int h = i / D, dd = i - h * D;
-        const float sum = ((s_o[0][h][dd] + s_o[1][h][dd]) + s_o[2][h][dd]) + s_o[3][h][dd];
-        a.part_o[((size_t)split * (a.Hkv * kAttnG) + hq0 + h) * D + dd] = sum;
-    }
-    if (tid < kAttnG) {
-        float *ml = a.part_ml + ((size_t)split * (a.Hkv * kAttnG) + hq0 + tid) * 2;
-        ml[0] = s_m[tid];
-        ml[1] = s_l[tid];
+        const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));  // finite
+        float o = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float c = s_m[w][h] == -INFINITY ? 0.f : exp2f(s_m[w][h] - M);
+            o += c * s_o[w][h][dd];
+            l += c * s_l[w][h];
+        }
+        a.part_o[((size_t)split * Hq + hq0 + h) * D + dd] = o;
+        if (dd == 0) {
+            float *ml = a.part_ml + ((size_t)split * Hq + hq0 + h) * 2;
+            ml[0] = M;
+            ml[1] = l;
+        }
     }
 }
 
-// one block per query head, one thread per dim
-__global__ __launch_bounds__(256) void gqa_combine_kernel(const float *__restrict__ part_o,
-                                                          const float *__restrict__ part_ml, int Hq, int D,
-                                                          int nsplit, uint16_t *__restrict__ out)
+// grid (Hq, D / 16): thread (j, d) sums splits j, j + 16, ... of dim d of
+// block.y's 16 dims; the 16 sums are added in order.  Every global load
+// (the splits' max and weight sum, and up to 16 partial outputs per thread)
+// is issued before the first reduction, so the kernel waits on memory about
+// once.
+constexpr int kCombinePerThread = 16;
+
+__global__ __launch_bounds__(kAttnCombineThreads) void gqa_combine_kernel(const float *__restrict__ part_o,
+                                                                          const float *__restrict__ part_ml, int Hq,
+                                                                          int D, int nsplit,
+                                                                          uint16_t *__restrict__ out)
 {
-    const int h = blockIdx.x, i = threadIdx.x;
-    if (i >= D) return;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((size_t)s * Hq + h) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float c = exp2f(part_ml[((size_t)s * Hq + h) * 2] - M);
-        den += c * part_ml[((size_t)s * Hq + h) * 2 + 1];
-        num += c * part_o[((size_t)s * Hq + h) * D + i];
+    constexpr int kML = kAttnMaxSplits / kAttnCombineThreads;  // (max, sum) pairs per thread
+    __shared__ float s_c[kAttnMaxSplits];
+    __shared__ float s_red[2][4];
+    __shared__ float s_num[16][17];
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = tid >> 4, dl = tid & 15, d = 16 * blockIdx.y + dl;
+
+    float2 ml[kML];
+#pragma unroll
+    for (int i = 0; i < kML; ++i) {
+        const int s = tid + kAttnCombineThreads * i;
+        ml[i] = s < nsplit ? *reinterpret_cast<const float2 *>(part_ml + ((size_t)s * Hq + h) * 2)
+                           : make_float2(-INFINITY, 0.f);
     }
-    out[(size_t)h * D + i] = f32_to_bf16(num / den);
+    float po[kCombinePerThread];
+#pragma unroll
+    for (int i = 0; i < kCombinePerThread; ++i) {
+        const int s = j + 16 * i;
+        po[i] = s < nsplit ? part_o[((size_t)s * Hq + h) * D + d] : 0.f;
+    }
+
+    float m = ml[0].x;
+#pragma unroll
+    for (int i = 1; i < kML; ++i) m = fmaxf(m, ml[i].x);
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) m = fmaxf(m, __shfl_xor(m, w));
+    if (lane == 0) s_red[0][wave] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));  // finite
+
+    float den = 0.f;
+#pragma unroll
+    for (int i = 0; i < kML; ++i) {
+        const int s = tid + kAttnCombineThreads * i;
+        if (s < nsplit) {
+            const float c = exp2f(ml[i].x - M);
+            s_c[s] = c;
+            den += c * ml[i].y;
+        }
+    }
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) den += __shfl_xor(den, w);
+    if (lane == 0) s_red[1][wave] = den;
+    __syncthreads();
+    den = ((s_red[1][0] + s_red[1][1]) + s_red[1][2]) + s_red[1][3];
+
+    float num = 0.f;
+#pragma unroll
+    for (int i = 0; i < kCombinePerThread; ++i) {
+        const int s = j + 16 * i;
+        if (s < nsplit) num += s_c[s] * po[i];
+    }
+    for (int s = j + 16 * kCombinePerThread; s < nsplit; s += 16)  // more than 256 splits
+        num += s_c[s] * part_o[((size_t)s * Hq + h) * D + d];
+    s_num[j][dl] = num;
+    __syncthreads();
+    if (tid < 16) {
+        float t = 0.f;
+        for (int i = 0; i < 16; ++i) t += s_num[i][tid];
+        out[(size_t)h * D + 16 * blockIdx.y + tid] = f32_to_bf16(t / den);
+    }
 }
 
-// tokens per block: a power of two, 64 .. 1024, about 1024 blocks in the grid
-int attn_chunk(int Hkv, int L)
+// Splits per KV head: at most kAttnMaxSplits and at most one per 128 tokens.
+static int attn_max_splits(int L)
 {
-    const int64_t want = ((int64_t)L * Hkv + 1023) / 1024;
-    int c = 64;
-    while (c < want && c < 1024) c <<= 1;
-    return c;
+    return (int)std::min<int64_t>(kAttnMaxSplits, ((int64_t)L + 127) / 128);
 }
 
 size_t attn_workspace_bytes(int Hq, int Hkv, int D, int L)
 {
-    const int64_t ns = (L + attn_chunk(Hkv, L) - 1) / attn_chunk(Hkv, L);
-    return (size_t)ns * Hq * (D + 2) * 4;
+    (void)Hkv;
+    return (size_t)attn_max_splits(L) * Hq * (D + 2) * 4;
+}
+
+// Blocks of gqa_partial_kernel<D> that the device runs at once (occupancy
+// per CU times CUs), queried once per device and D.
+template <int D>
+static int attn_resident_blocks()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gqa_partial_kernel<D>, kAttnThreads, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    v = per_cu * cus;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+int attn_chunk(int Hkv, int L, int resident)
+{
+    const int want = std::max(1, std::min(attn_max_splits(L), (resident + Hkv - 1) / Hkv));
+    const int64_t per = ((int64_t)L + want - 1) / want;
+    return (int)((per + 127) / 128 * 128);
 }
 
 hipError_t launch_gqa_decode(int Hq, int Hkv, int D, int L, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, void *ws, hipStream_t s, EventTrace *tr)
 {
+    const int resident = D == 64 ? attn_resident_blocks<64>()
+                         : D == 128 ? attn_resident_blocks<128>() : attn_resident_blocks<256>();
     AttnArgs a;
     a.q = q; a.k = k; a.v = v;
     a.Hkv = Hkv; a.L = L;
-    a.C = attn_chunk(Hkv, L);
-    a.nsplit = (L + a.C - 1) / a.C;
+    a.C = attn_chunk(Hkv, L, resident);
+    a.nsplit = (L + a.C - 1) / a.C;  // <= attn_max_splits(L), since C >= max(128, L / max splits)
     a.scale2 = 1.4426950408889634f / sqrtf((float)D);
     a.part_o = static_cast<float *>(ws);
     a.part_ml = a.part_o + (size_t)a.nsplit * Hq * D;
@@ -286,8 +365,8 @@ hipError_t launch_gqa_decode(int Hq, int Hkv, int D, int L, const uint16_t *q, c
     case 128: launch(tr, gqa_partial_kernel<128>, grid, dim3(kAttnThreads), 0, s, a); break;
     default: launch(tr, gqa_partial_kernel<256>, grid, dim3(kAttnThreads), 0, s, a); break;
     }
-    launch(tr, gqa_combine_kernel, dim3(Hq), dim3(256), 0, s, (const float *)a.part_o, (const float *)a.part_ml,
-           Hq, D, a.nsplit, o);
+    launch(tr, gqa_combine_kernel, dim3(Hq, D / 16), dim3(kAttnCombineThreads), 0, s, (const float *)a.part_o,
+           (const float *)a.part_ml, Hq, D, a.nsplit, o);
     return hipGetLastError();
 }
 

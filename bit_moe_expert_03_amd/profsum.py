@@ -13,7 +13,7 @@
 Usage (from the repository root):
     python -m bit_moe_expert_03_amd.profsum trace DB --cmd "..." --title "..."
     python -m bit_moe_expert_03_amd.profsum traffic --fetch DIR --write DIR \\
-        --copy-kernel SUBSTRING --copy-bytes N --kernel NAME=SRC[,SRC...] ... --out FILE.json
+        --copy-kernel SUBSTRING --copy-bytes N --kernel NAME=SRC[,SRC...] ... --out FILE.json [--merge]
   NAME: KEY or KEY@MATCH; MATCH (default KEY) is a substring of exactly one
   "kernel [grid N]" name (N workgroups), so a kernel launched with several
   grids needs its grid in MATCH; KEY names the entry in the JSON.
@@ -117,6 +117,15 @@ def cmd_traffic(a):
     wscale = a.copy_bytes / (cw * 1024.0)
     out = {"copy_kernel": cname, "copy_bytes": a.copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale": fscale, "write_scale": wscale, "kernels": {}}
+    if a.merge and os.path.exists(a.out):
+        # keep the rows of an earlier run (each carries its own scales); rows
+        # named again here are replaced
+        with open(a.out) as fh:
+            old = json.load(fh)
+        for key, row in old.get("kernels", {}).items():
+            row.setdefault("fetch_scale", old.get("fetch_scale"))
+            row.setdefault("write_scale", old.get("write_scale"))
+            out["kernels"][key] = row
     for spec in a.kernel:
         name, srcs = spec.split("=", 1)
         srcs = srcs.split(",")
@@ -124,6 +133,7 @@ def cmd_traffic(a):
         f, full = pick(fetch, match or key)
         w, _ = pick(write, match or key)
         out["kernels"][key] = {"matched": full, "fetch_kib": f, "write_kib": w,
+                                "fetch_scale": fscale, "write_scale": wscale,
                                 "fetch_bytes": f * 1024.0 * fscale, "write_bytes": w * 1024.0 * wscale,
                                 "traffic_bytes": f * 1024.0 * fscale + w * 1024.0 * wscale,
                                 "sources": srcs, "source_sha256": source_hash(srcs)}
@@ -146,6 +156,7 @@ def main(argv=None):
     f.add_argument("--copy-bytes", type=int, required=True)
     f.add_argument("--kernel", action="append", required=True)
     f.add_argument("--out", required=True)
+    f.add_argument("--merge", action="store_true", help="keep the rows already in --out that are not named here")
     a = ap.parse_args(argv)
     {"trace": cmd_trace, "traffic": cmd_traffic}[a.what](a)
 
