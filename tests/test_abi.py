@@ -213,3 +213,17 @@ def test_gqa_workspace_and_argument_checks():
     assert b"overlap" in L.moe_last_error()
     ev = (ctypes.c_void_p * 3)()
     assert L.moe_gqa_decode_timed(ctypes.byref(a), *args, need, None, ev, 3) == B.MOE_ERR_ARG
+
+
+def test_fewrow_parity_cases_have_fewrow_experts():
+    """The GPU parity cases named fewrow_* route many experts to one or two
+    rows and some to three or more."""
+    import oracle
+    import test_gpu_parity as P
+    for name, (dims, zipf) in P.SMALL.items():
+        if not name.startswith("fewrow_"):
+            continue
+        c = wl.make_case(dims, seed=100 + list(P.SMALL).index(name), zipf=zipf, weights=False)
+        counts = oracle.route(c["logits"], dims.k, 32)["counts"]
+        assert ((counts >= 1) & (counts <= 2)).sum() >= 10, name
+        assert (counts >= 3).sum() >= 1, name

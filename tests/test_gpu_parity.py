@@ -42,6 +42,13 @@ SMALL = {
     # K split into two ranges (d = 1024) and without (d = 256)
     "T37_E30_d1024_ksplit": (wl.Dims(T=37, d=1024, E=30, k=4, F=64, Fs=64, G=64), False),
     "T37_E13_k3": (wl.Dims(T=37, d=256, E=13, k=3, F=64, Fs=64, G=32), False),
+    # many experts with one or two rows next to experts with more (the tail
+    # of a skewed batch: one-row tiles on the matrix cores), at d = 2048,
+    # F = 192, G = 128, and with down blocks chained over column blocks
+    "fewrow_T40_E128_k2": (wl.Dims(T=40, d=256, E=128, k=2, F=128, Fs=64, G=32), False),
+    "fewrow_T36_E64_k4_d2048": (wl.Dims(T=36, d=2048, E=64, k=4, F=64, Fs=64, G=64), False),
+    "fewrow_T48_E96_k2_F192": (wl.Dims(T=48, d=1024, E=96, k=2, F=192, Fs=128, G=64), False),
+    "fewrow_T40_E128_k2_G128": (wl.Dims(T=40, d=256, E=128, k=2, F=128, Fs=128, G=128), False),
 }
 
 
@@ -196,6 +203,7 @@ CHAINED = {
     "chain_T300_d1024_F128": wl.Dims(T=300, d=1024, E=16, k=4, F=128, Fs=128, G=64),
     "chain_T90_d1024_F256_G32": wl.Dims(T=90, d=1024, E=8, k=2, F=256, Fs=256, G=32),
     "chain_T40_d512_F512_G128": wl.Dims(T=40, d=512, E=4, k=3, F=512, Fs=512, G=128),
+    "chain_fewrow_T40_d1024_E128": wl.Dims(T=40, d=1024, E=128, k=2, F=128, Fs=128, G=64),
 }
 
 
