@@ -113,10 +113,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
     for (int i = 0; i < DPL; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int base = kAttnSlice * wave; base < n; base += 4 * kAttnSlice) {
-        // K rows of the two 16-token tiles (row r of tile j = token base + 16 j + r);
-        // past the block's last token, the last valid row is read and its score masked
-        uint4 kr[2][KK];
+    // K rows of the two 16-token tiles of a slice (row r of tile j = token
+    // base + 16 j + r); past the block's last token, the last valid row is
+    // read and its score masked.  Up to D = 128 the next slice's K rows are
+    // loaded into the same registers as soon as the score MFMAs have read
+    // them, so they arrive under this slice's softmax and output work (at
+    // D = 256 that would not fit the registers of two blocks per CU).
+    constexpr bool kPrefetchK = D <= 128;
+    uint4 kr[2][KK];
+    auto load_k = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int t = min(base + 16 * j + r, n - 1);
@@ -124,6 +129,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
             for (int kk = 0; kk < KK; ++kk)
                 kr[j][kk] = load_stream4(kb + (size_t)t * D + 32 * kk + 8 * grp);
         }
+    };
+    if (kPrefetchK && kAttnSlice * wave < n) load_k(kAttnSlice * wave);
+    for (int base = kAttnSlice * wave; base < n; base += 4 * kAttnSlice) {
+        if (!kPrefetchK) load_k(base);
         // V of tokens tau(grp, k), dims DPL r .. DPL r + DPL - 1
         uint32_t vw[8][VW];
 #pragma unroll
@@ -150,6 +159,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) sc[j] = mfma16(kr[j][kk], qb[kk], sc[j]);
         }
+        if (kPrefetchK && base + 4 * kAttnSlice < n) load_k(base + 4 * kAttnSlice);
         float s[8];
         float mx = -INFINITY;
 #pragma unroll
