@@ -289,8 +289,11 @@ MOE_API size_t moe_gqa_workspace_bytes(const moe_attn_dims *dims);
 /* q bf16 [Hq][D]; k, v bf16 [Hkv][L][D] (one row per cached token); o bf16
  * [Hq][D], caller-owned; ws: moe_gqa_workspace_bytes() bytes, any contents
  * (fully rewritten by each call).  Two kernels on `stream` (context splits,
- * then their combination); results are deterministic.  o must not overlap
- * the inputs or ws.  Invalid arguments return a status with nothing enqueued. */
+ * then their combination in a fixed order).  The split count follows the
+ * device (its co-resident block count), so results are bit-identical from
+ * call to call on one kind of GPU and may differ in the last bits between
+ * kinds.  o must not overlap the inputs or ws.  Invalid arguments return a
+ * status with nothing enqueued. */
 MOE_API moe_status moe_gqa_decode(const moe_attn_dims *dims, const uint16_t *q, const uint16_t *k,
                                   const uint16_t *v, uint16_t *o, void *ws, size_t ws_bytes, void *stream);
 
