@@ -275,7 +275,8 @@ MOE_API const char *moe_last_error(void);
  * row is read from memory once for its eight heads.  The pages do not write
  * the formula; this is scaled dot-product attention:
  *   o[h] = sum_t softmax_t(q[h] . k[g][t] / sqrt(D)) v[g][t],  g = h / 8,
- * fp32 arithmetic from bf16 inputs, o rounded to bf16 (nearest even).
+ * fp32 arithmetic from bf16 inputs (finite: non-finite q, k or v are outside
+ * the contract), o rounded to bf16 (nearest even).
  * Supported: Hkv >= 1, Hq = 8 * Hkv, Hq <= 1024; D in {64, 128, 256};
  * 1 <= L <= 2^24. */
 typedef struct {
