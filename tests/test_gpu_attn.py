@@ -27,7 +27,8 @@ pytestmark = pytest.mark.gpu
 A = wl.AttnDims
 # ragged lengths (one token, fewer tokens than a block takes, a last block of
 # 1 or of a few tokens), every head dimension, one KV head and the most KV
-# heads the entry point takes, and block sizes from 64 to 1024 tokens
+# heads the entry point takes, and splits from 128 to several hundred tokens
+# (multiples of 128 and, for long ones, of 32)
 SMALL = {
     "L1_D128": A(Hq=8, Hkv=1, D=128, L=1),
     "L5_D64_Hkv2": A(Hq=16, Hkv=2, D=64, L=5),
@@ -36,9 +37,13 @@ SMALL = {
     "L1000_D64_Hkv3": A(Hq=24, Hkv=3, D=64, L=1000),
     "L3000_D256_Hkv2": A(Hq=16, Hkv=2, D=256, L=3000),
     "Hkv128_L200_D64": A(Hq=1024, Hkv=128, D=64, L=200),
-    "L70001_chunk128": A(Hq=8, Hkv=1, D=128, L=70001),
-    "L600001_chunk1024_D64": A(Hq=8, Hkv=1, D=64, L=600001),
-    "L300001_chunk512_D256": A(Hq=8, Hkv=1, D=256, L=300001),
+    "L70001_D128": A(Hq=8, Hkv=1, D=128, L=70001),
+    "L600001_D64": A(Hq=8, Hkv=1, D=64, L=600001),
+    "L300001_D256": A(Hq=8, Hkv=1, D=256, L=300001),
+    # the most KV heads with a long context, and D = 256 (its kernel keeps
+    # the K loads at the top of each slice) at a long ragged length
+    "Hkv128_L4096_D128": A(Hq=1024, Hkv=128, D=128, L=4096),
+    "L100003_D256_Hkv2": A(Hq=16, Hkv=2, D=256, L=100003),
 }
 
 
