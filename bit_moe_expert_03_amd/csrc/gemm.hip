@@ -793,7 +793,10 @@ static int down_chain(const Plan &p, int BM, int ntn)
     const int nk = p.F / kKStep;
     if (p.d % 256 != 0 || p.F != p.Fs || nk < 2 || (nk & (nk - 1)) != 0) return 1;
     if (p.down_nc >= 1 && ntn % p.down_nc == 0) return p.down_nc;
+    // chains of 4 where the grid still holds four rounds of blocks (T = 32768:
+    // down 772 -> 751 us), of 2 where it holds two (T = 4096), else none (T = 512)
     const int64_t tiles = (p.A + BM - 1) / BM + (p.T + BM - 1) / BM;
+    if (ntn % 4 == 0 && tiles * (ntn / 4) >= 4 * 512) return 4;
     return (ntn % 2 == 0 && tiles * (ntn / 2) >= 2 * 512) ? 2 : 1;
 }
 
