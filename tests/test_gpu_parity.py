@@ -145,6 +145,27 @@ def test_layer_small_shapes_all_tokens(name):
         check_y(c, g, ref)
 
 
+# the largest dimensions the entry points take: d, F and Fs up to 16384 and
+# k = E = 256, on the decode path (T <= 32) and on the GEMM path (T = 33)
+MAXDIMS = {
+    "max_d_decode": wl.Dims(T=1, d=16384, E=256, k=8, F=64, Fs=64, G=64),
+    "max_d_gemm": wl.Dims(T=33, d=16384, E=256, k=8, F=64, Fs=64, G=64),
+    "max_F_decode": wl.Dims(T=1, d=128, E=4, k=2, F=16384, Fs=16384, G=128),
+    "max_F_gemm": wl.Dims(T=33, d=256, E=4, k=2, F=16384, Fs=16384, G=128),
+    "k_eq_E_256_decode": wl.Dims(T=2, d=64, E=256, k=256, F=64, Fs=64, G=64),
+    "k_eq_E_256_gemm": wl.Dims(T=33, d=64, E=256, k=256, F=64, Fs=64, G=64),
+}
+
+
+@pytest.mark.parametrize("name", list(MAXDIMS))
+def test_layer_maximum_dims_all_tokens(name):
+    dims = MAXDIMS[name]
+    c = wl.make_case(dims, seed=400 + list(MAXDIMS).index(name))
+    g = run(c)
+    ref = check_routing(c, g)
+    check_y(c, g, ref)
+
+
 @pytest.mark.parametrize("name", [n for n in SMALL if SMALL[n][0].T >= 2])
 def test_layer_small_shapes_tile128(name):
     """Every small shape with 128-row tiles (the four-sub-tile GEMM bodies)."""
