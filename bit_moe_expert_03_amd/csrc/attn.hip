@@ -77,6 +77,11 @@ __device__ __forceinline__ uint2 load_stream2(const uint16_t *p)
     return make_uint2(v[0], v[1]);
 }
 
+// 2^x by the hardware instruction alone: no rescaling for results below
+// 2^-126, which come out as 0.  For softmax weights (x <= 0 against the
+// running max) that drops only weights under 2^-126 of the largest one.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_new == m_run ? 1.f : exp2f(m_run - m_new);  // 1 while nothing is valid
+        const float alpha = m_new == m_run ? 1.f : exp2_fast(m_run - m_new);  // 1 while nothing is valid
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
             for (int i = 0; i < DPL; ++i) oacc[i] *= alpha;
@@ -184,8 +189,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
         uint32_t ph[4], pl[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const float p0 = s[2 * w] == -INFINITY ? 0.f : exp2f(s[2 * w] - m_new);
-            const float p1 = s[2 * w + 1] == -INFINITY ? 0.f : exp2f(s[2 * w + 1] - m_new);
+            const float p0 = s[2 * w] == -INFINITY ? 0.f : exp2_fast(s[2 * w] - m_new);
+            const float p1 = s[2 * w + 1] == -INFINITY ? 0.f : exp2_fast(s[2 * w + 1] - m_new);
             l_run += p0 + p1;
             ph[w] = pack_bf16x2(p0, p1);
             pl[w] = pack_bf16x2(p0 - __uint_as_float(ph[w] << 16), p1 - __uint_as_float(ph[w] & 0xFFFF0000u));
@@ -200,7 +205,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const uint32_t x = vw[2 * w][nt >> 1], y = vw[2 * w + 1][nt >> 1];
-                av[w] = (nt & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+                // (low halves of x, y) or (high halves of x, y): one byte permute
+                av[w] = (nt & 1) ? __builtin_amdgcn_perm(y, x, 0x07060302u) : __builtin_amdgcn_perm(y, x, 0x05040100u);
             }
             const uint4 au = make_uint4(av[0], av[1], av[2], av[3]);
             oacc[nt] = mfma16(au, bh, oacc[nt]);
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
         float o = 0.f, l = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const float c = s_m[w][h] == -INFINITY ? 0.f : exp2f(s_m[w][h] - M);
+            const float c = s_m[w][h] == -INFINITY ? 0.f : exp2_fast(s_m[w][h] - M);
             o += c * s_o[w][h][dd];
             l += c * s_l[w][h];
         }
