@@ -50,7 +50,6 @@ namespace moe {
 
 constexpr int kAttnG = 8;            // query heads per KV head
 constexpr int kAttnThreads = 256;    // 4 waves
-constexpr int kAttnSlice = 32;       // tokens per wave iteration
 constexpr int kAttnMaxSplits = 1024;
 constexpr int kAttnCombineThreads = 256;
 
@@ -88,9 +87,23 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c)
                                                    c, 0, 0, 0);
 }
 
-template <int D>
+// v_mfma_f32_16x16x16_bf16: the same lane layout with 4 contraction slots per lane
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16k16(uint2 a, uint2 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
+                                                     c, 0, 0, 0);
+}
+
+// NJ: 16-token score tiles per wave slice (slices of 16 NJ tokens; the
+// output MFMA contracts over the slice: 16x16x32 for NJ = 2, 16x16x16 for
+// NJ = 1, which short contexts take to put twice as many waves to work)
+template <int D, int NJ>
 __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a)
 {
+    constexpr int SL = 16 * NJ;  // tokens per wave slice
+    constexpr int TL = 4 * NJ;   // tokens per lane in the output MFMA's K block
+    constexpr int PW = 2 * NJ;   // words per lane of a weight operand
     constexpr int DPL = D / 16;  // head dims per lane in the output tiles (= number of tiles)
     constexpr int VW = DPL / 2;  // words of V per lane and token
     constexpr int KK = D / 32;   // score MFMAs per 16-token tile
@@ -125,23 +138,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
     // them, so they arrive under this slice's softmax and output work (at
     // D = 256 that would not fit the registers of two blocks per CU).
     constexpr bool kPrefetchK = D <= 128;
-    uint4 kr[2][KK];
+    uint4 kr[NJ][KK];
     auto load_k = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int t = min(base + 16 * j + r, n - 1);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
                 kr[j][kk] = load_stream4(kb + (size_t)t * D + 32 * kk + 8 * grp);
         }
     };
-    if (kPrefetchK && kAttnSlice * wave < n) load_k(kAttnSlice * wave);
-    for (int base = kAttnSlice * wave; base < n; base += 4 * kAttnSlice) {
+    if (kPrefetchK && SL * wave < n) load_k(SL * wave);
+    for (int base = SL * wave; base < n; base += 4 * SL) {
         if (!kPrefetchK) load_k(base);
         // V of tokens tau(grp, k), dims DPL r .. DPL r + DPL - 1
-        uint32_t vw[8][VW];
+        uint32_t vw[TL][VW];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < TL; ++k) {
             const int t = min(base + 16 * (k >> 2) + 4 * grp + (k & 3), n - 1);
             const uint16_t *src = vb + (size_t)t * D + DPL * r;
             if constexpr (VW == 2) {
@@ -157,18 +170,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
         }
 
         // scores: lane holds head r, tokens base + 16 j + 4 grp + i
-        f32x4 sc[2];
+        f32x4 sc[NJ];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) sc[j] = mfma16(kr[j][kk], qb[kk], sc[j]);
         }
-        if (kPrefetchK && base + 4 * kAttnSlice < n) load_k(base + 4 * kAttnSlice);
-        float s[8];
+        if (kPrefetchK && base + 4 * SL < n) load_k(base + 4 * SL);
+        float s[TL];
         float mx = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < TL; ++k) {
             const int t = base + 16 * (k >> 2) + 4 * grp + (k & 3);
             s[k] = (head_ok && t < n) ? sc[k >> 2][k & 3] * a.scale2 : -INFINITY;
             mx = fmaxf(mx, s[k]);
@@ -186,31 +199,34 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
 
         // weights and their bf16 hi / lo parts: B operand of the output MFMAs
         // (K position k = token tau(grp, k))
-        uint32_t ph[4], pl[4];
+        uint32_t ph[PW], pl[PW];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < PW; ++w) {
             const float p0 = s[2 * w] == -INFINITY ? 0.f : exp2_fast(s[2 * w] - m_new);
             const float p1 = s[2 * w + 1] == -INFINITY ? 0.f : exp2_fast(s[2 * w + 1] - m_new);
             l_run += p0 + p1;
             ph[w] = pack_bf16x2(p0, p1);
             pl[w] = pack_bf16x2(p0 - __uint_as_float(ph[w] << 16), p1 - __uint_as_float(ph[w] & 0xFFFF0000u));
         }
-        const uint4 bh = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-        const uint4 bl = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-
-        // output tiles: A operand of tile nt = dim DPL r + nt of tokens tau(grp, 0..7)
+        // output tiles: A operand of tile nt = dim DPL r + nt of tokens tau(grp, 0..TL-1)
 #pragma unroll
         for (int nt = 0; nt < DPL; ++nt) {
-            uint32_t av[4];
+            uint32_t av[PW];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < PW; ++w) {
                 const uint32_t x = vw[2 * w][nt >> 1], y = vw[2 * w + 1][nt >> 1];
                 // (low halves of x, y) or (high halves of x, y): one byte permute
                 av[w] = (nt & 1) ? __builtin_amdgcn_perm(y, x, 0x07060302u) : __builtin_amdgcn_perm(y, x, 0x05040100u);
             }
-            const uint4 au = make_uint4(av[0], av[1], av[2], av[3]);
-            oacc[nt] = mfma16(au, bh, oacc[nt]);
-            oacc[nt] = mfma16(au, bl, oacc[nt]);
+            if constexpr (NJ == 2) {
+                const uint4 au = make_uint4(av[0], av[1], av[2], av[3]);
+                oacc[nt] = mfma16(au, make_uint4(ph[0], ph[1], ph[2], ph[3]), oacc[nt]);
+                oacc[nt] = mfma16(au, make_uint4(pl[0], pl[1], pl[2], pl[3]), oacc[nt]);
+            } else {
+                const uint2 au = make_uint2(av[0], av[1]);
+                oacc[nt] = mfma16k16(au, make_uint2(ph[0], ph[1]), oacc[nt]);
+                oacc[nt] = mfma16k16(au, make_uint2(pl[0], pl[1]), oacc[nt]);
+            }
         }
     }
 
@@ -323,10 +339,10 @@ __global__ __launch_bounds__(kAttnCombineThreads) void gqa_combine_kernel(const 
     }
 }
 
-// Splits per KV head: at most kAttnMaxSplits and at most one per 128 tokens.
+// Splits per KV head: at most kAttnMaxSplits and at most one per 64 tokens.
 static int attn_max_splits(int L)
 {
-    return (int)std::min<int64_t>(kAttnMaxSplits, ((int64_t)L + 127) / 128);
+    return (int)std::min<int64_t>(kAttnMaxSplits, ((int64_t)L + 63) / 64);
 }
 
 size_t attn_workspace_bytes(int Hq, int Hkv, int D, int L)
@@ -335,9 +351,9 @@ size_t attn_workspace_bytes(int Hq, int Hkv, int D, int L)
     return (size_t)attn_max_splits(L) * Hq * (D + 2) * 4;
 }
 
-// Blocks of gqa_partial_kernel<D> that the device runs at once (occupancy
-// per CU times CUs), queried once per device and D.
-template <int D>
+// Blocks of gqa_partial_kernel<D, NJ> that the device runs at once
+// (occupancy per CU times CUs), queried once per device and variant.
+template <int D, int NJ>
 static int attn_resident_blocks()
 {
     static std::atomic<int> cache[64];
@@ -346,7 +362,8 @@ static int attn_resident_blocks()
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v > 0) return v;
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gqa_partial_kernel<D>, kAttnThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gqa_partial_kernel<D, NJ>, kAttnThreads, 0) !=
+            hipSuccess ||
         per_cu < 1)
         per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
@@ -355,37 +372,61 @@ static int attn_resident_blocks()
     return v;
 }
 
-int attn_chunk(int Hkv, int L, int resident)
+int attn_chunk(int Hkv, int L, int resident, int round)
 {
     const int want = std::max(1, std::min(attn_max_splits(L), (resident + Hkv - 1) / Hkv));
     const int64_t per = ((int64_t)L + want - 1) / want;
-    // A split that is not a multiple of 128 tokens leaves its waves one
-    // 32-token slice apart.  Long splits (512 tokens and more) take that for
-    // a grid that fills the device more closely (L = 131072: 748 blocks
-    // instead of 684, 6.0 against 5.7 TB/s); short ones keep whole rounds of
-    // slices (L = 32768, 2 slices per wave: 14.4 against 15.2 us).
-    const int64_t quantum = per >= 512 ? 32 : 128;
-    return (int)std::max<int64_t>(128, (per + quantum - 1) / quantum * quantum);
+    // A split that is not a multiple of a round (the block's four slices)
+    // leaves its waves one slice apart.  Long splits (512 tokens and more)
+    // take that for a grid that fills the device more closely (L = 131072:
+    // 748 blocks instead of 684, 6.0 against 5.7 TB/s); short ones keep
+    // whole rounds (L = 32768, 2 slices per wave: 14.4 against 15.2 us).
+    const int64_t quantum = per >= 512 ? 32 : round;
+    return (int)std::max<int64_t>(round, (per + quantum - 1) / quantum * quantum);
+}
+
+template <int D>
+static void launch_partial(EventTrace *tr, int nj, dim3 grid, hipStream_t s, const AttnArgs &a)
+{
+    if (nj == 1)
+        launch(tr, gqa_partial_kernel<D, 1>, grid, dim3(kAttnThreads), 0, s, a);
+    else
+        launch(tr, gqa_partial_kernel<D, 2>, grid, dim3(kAttnThreads), 0, s, a);
+}
+
+template <int D>
+static int attn_plan(int Hkv, int L, int *nj)
+{
+    // 32-token slices; where that gives each wave a single slice and leaves
+    // the grid short of the co-resident block count (short contexts), 16-token
+    // slices put twice as many waves to work, each with half the arithmetic
+    const int resident2 = attn_resident_blocks<D, 2>();
+    const int c2 = attn_chunk(Hkv, L, resident2, 128);
+    if (c2 == 128 && (int64_t)((L + 127) / 128) * Hkv < resident2) {
+        *nj = 1;
+        return attn_chunk(Hkv, L, attn_resident_blocks<D, 1>(), 64);
+    }
+    *nj = 2;
+    return c2;
 }
 
 hipError_t launch_gqa_decode(int Hq, int Hkv, int D, int L, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, void *ws, hipStream_t s, EventTrace *tr)
 {
-    const int resident = D == 64 ? attn_resident_blocks<64>()
-                         : D == 128 ? attn_resident_blocks<128>() : attn_resident_blocks<256>();
+    int nj = 2;
     AttnArgs a;
     a.q = q; a.k = k; a.v = v;
     a.Hkv = Hkv; a.L = L;
-    a.C = attn_chunk(Hkv, L, resident);
-    a.nsplit = (L + a.C - 1) / a.C;  // <= attn_max_splits(L), since C >= max(128, L / max splits)
+    a.C = D == 64 ? attn_plan<64>(Hkv, L, &nj) : D == 128 ? attn_plan<128>(Hkv, L, &nj) : attn_plan<256>(Hkv, L, &nj);
+    a.nsplit = (L + a.C - 1) / a.C;  // <= attn_max_splits(L), since C >= max(64, L / max splits)
     a.scale2 = 1.4426950408889634f / sqrtf((float)D);
     a.part_o = static_cast<float *>(ws);
     a.part_ml = a.part_o + (size_t)a.nsplit * Hq * D;
     const dim3 grid(a.nsplit, Hkv);
     switch (D) {
-    case 64: launch(tr, gqa_partial_kernel<64>, grid, dim3(kAttnThreads), 0, s, a); break;
-    case 128: launch(tr, gqa_partial_kernel<128>, grid, dim3(kAttnThreads), 0, s, a); break;
-    default: launch(tr, gqa_partial_kernel<256>, grid, dim3(kAttnThreads), 0, s, a); break;
+    case 64: launch_partial<64>(tr, nj, grid, s, a); break;
+    case 128: launch_partial<128>(tr, nj, grid, s, a); break;
+    default: launch_partial<256>(tr, nj, grid, s, a); break;
     }
     launch(tr, gqa_combine_kernel, dim3(Hq, D / 16), dim3(kAttnCombineThreads), 0, s, (const float *)a.part_o,
            (const float *)a.part_ml, Hq, D, a.nsplit, o);

@@ -90,9 +90,10 @@ hipError_t launch_decode(const Plan &p, const float *logits, const uint16_t *x,
                          hipStream_t s, EventTrace *tr = nullptr);
 
 // ---- attn.hip: decode attention over grouped KV heads (8 query heads per KV head)
-// tokens per block (at least 128, a multiple of 32) for `resident` co-resident blocks
-int attn_chunk(int Hkv, int L, int resident);
-// bound over every device: at most min(1024, ceil(L / 128)) splits per KV head
+// tokens per block (at least `round`, the four slices of a block, and a
+// multiple of it or of 32) for `resident` co-resident blocks
+int attn_chunk(int Hkv, int L, int resident, int round);
+// bound over every device: at most min(1024, ceil(L / 64)) splits per KV head
 size_t attn_workspace_bytes(int Hq, int Hkv, int D, int L);
 hipError_t launch_gqa_decode(int Hq, int Hkv, int D, int L, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, void *ws, hipStream_t s, EventTrace *tr = nullptr);

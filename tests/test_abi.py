@@ -187,8 +187,8 @@ def test_gqa_workspace_and_argument_checks():
     L = B.lib()
     a = B.make_attn_dims(wl.ATTN_CONFIGS["attn_L32768"])
     need = B.moe_gqa_workspace_bytes(a)
-    # 4 KV heads x 32768 tokens over ~1024 blocks: 128 tokens per split, 256 splits
-    assert need == 256 * 32 * (128 + 2) * 4
+    # bound over every device: min(1024, ceil(L / 64)) splits of (o, max, sum) per query head
+    assert need == 512 * 32 * (128 + 2) * 4
     assert B.moe_gqa_workspace_bytes(B.moe_attn_dims(32, 4, 128, 1)) == 1 * 32 * 130 * 4
     for bad in [(33, 4, 128, 64), (32, 4, 96, 64), (32, 4, 128, 0), (0, 0, 128, 64), (8 * 129, 129, 64, 8),
                 (32, 4, 128, (1 << 24) + 1)]:
