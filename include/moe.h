@@ -18,15 +18,19 @@
  *    travel as uint16_t bit patterns.  Every array is dense, row-major, and
  *    must be 16-byte aligned.  Inputs must not alias outputs.
  *  - The caller owns every buffer (inputs, outputs, workspace).  The library
- *    allocates nothing, keeps no state between calls, and is safe to call
- *    from several host threads on different streams.
+ *    allocates nothing and keeps no state between calls beyond a per-device
+ *    cache of the decode-attention kernels' co-resident block counts (queried
+ *    once) and the scratch array of moe_layer_noalloc; it is safe to call
+ *    from several host threads on different streams (except that calls of
+ *    moe_layer_noalloc that overlap on one GPU share its scratch array).
  *  - All compute calls are asynchronous on `stream` (a hipStream_t, or NULL
  *    for the default stream).  No call synchronises the host or copies data
  *    to the host.  Arguments are validated on the host before anything is
  *    enqueued: on a non-OK status nothing was enqueued and moe_last_error()
  *    tells why.  Faults inside kernels surface at the caller's next
  *    synchronisation.
- *  - Results are deterministic: identical inputs give identical bits.
+ *  - Results are deterministic: identical inputs give identical bits (for
+ *    moe_gqa_decode, on one kind of GPU: its split count follows the device).
  *
  * Weight layout (the pages give the format only as "groupwise affine 4-bit";
  * the layout is this library's choice): a matrix W[N_out][K_in] is
