@@ -15,29 +15,32 @@
 //   scores  S^T = K Q^T     v_mfma_f32_16x16x32_bf16: rows = 16 tokens,
 //                           columns = heads, K = head dims (bf16 products
 //                           are exact in fp32);
-//   output  O^T = V^T P^T   rows = 16 head dims, columns = heads, K = 32
-//                           tokens.  P is split into bf16 hi + lo parts
-//                           (two MFMAs), which keeps about 16 bits of each
-//                           weight, so the output carries fp32-level error.
+//   output  O^T = V^T P^T   rows = 16 head dims, columns = heads, K = the
+//                           slice's 32 tokens (v_mfma_f32_16x16x32_bf16) or
+//                           16 (v_mfma_f32_16x16x16_bf16).  P is split into
+//                           bf16 hi + lo parts (two MFMAs), which keeps about
+//                           16 bits of each weight, so the output carries
+//                           fp32-level error.
 // The score tile leaves lane l with head l % 16 and tokens 4 (l / 16) + i,
-// which is exactly a B operand of the output MFMA once the 32 tokens of two
-// score tiles are ordered tau(g, k) = 16 (k / 4) + 4 g + k % 4: the weights
-// never leave the lane.  V^T is formed in registers: lane (r, g) loads dims
-// D/16 r .. of its eight tokens tau(g, .) and interleaves them pairwise (one
-// bit-select per output word), so every A operand is one token-contiguous
-// column of V; row r of output tile n is head dim (D/16) r + n.
+// which is exactly a B operand of the output MFMA once the tokens of the
+// slice's score tiles are ordered tau(g, k) = 16 (k / 4) + 4 g + k % 4: the
+// weights never leave the lane.  V^T is formed in registers: lane (r, g)
+// loads dims D/16 r .. of its tokens tau(g, .) and interleaves them pairwise
+// (one byte permute per output word), so every A operand is one
+// token-contiguous column of V; row r of output tile n is head dim (D/16) r + n.
 //
 // Kernels (stream-ordered):
-//   gqa_partial_kernel<D>   grid (splits, Hkv), 4 waves, one round of blocks
-//                           (blocks per CU from the occupancy of the kernel
-//                           times the CUs); a block takes C consecutive
-//                           tokens (C >= 128, a multiple of 32), its waves take
-//                           interleaved 32-token slices, each with its own
-//                           online softmax (running max per head, rescale of
-//                           the accumulators when it grows), so the main
-//                           loop has no block barrier.  The four waves are
-//                           merged through LDS; writes the block's (max,
-//                           weight sum, unnormalised o) per query head.
+//   gqa_partial_kernel<D, NJ>  grid (splits, Hkv), 4 waves, one round of
+//                           blocks (blocks per CU from the occupancy of the
+//                           kernel times the CUs); a block takes C consecutive
+//                           tokens, its waves take interleaved slices of
+//                           16 NJ tokens (NJ = 2; NJ = 1 where a context is
+//                           too short to fill the grid otherwise), each with
+//                           its own online softmax (running max per head,
+//                           rescale of the accumulators when it grows), so
+//                           the main loop has no block barrier.  The four
+//                           waves are merged through LDS; writes the block's
+//                           (max, weight sum, unnormalised o) per query head.
 //   gqa_combine_kernel      grid (Hq, D/16): the splits' partials rescaled to
 //                           the global max and summed in a fixed order
 //                           (deterministic), o = sum / weight sum, bf16.
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gqa_partial_kernel(AttnArgs a
     for (int i = 0; i < DPL; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // K rows of the two 16-token tiles of a slice (row r of tile j = token
+    // K rows of the NJ 16-token tiles of a slice (row r of tile j = token
     // base + 16 j + r); past the block's last token, the last valid row is
     // read and its score masked.  Up to D = 128 the next slice's K rows are
     // loaded into the same registers as soon as the score MFMAs have read
